@@ -1,0 +1,496 @@
+// libfpd C ABI: argument checking, workspace planning, layouts, and the
+// launch sequences of the hot calls.  See include/fpd.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/fpd.h"
+#include "kernels.h"
+#include "layout.h"
+
+using namespace fpd;
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define FPD_TRY_HIP(expr)                                                           \
+  do {                                                                              \
+    hipError_t e_ = (expr);                                                         \
+    if (e_ != hipSuccess) return fail(FPD_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+int round8(int x) { return (x + 7) & ~7; }
+
+}  // namespace
+
+struct fpd_drafter {
+  fpd_config cfg;
+  fpd_weights w;
+  std::vector<fpd_layer_weights> layers;
+  RopeTab tab;
+  int esz;
+};
+
+struct fpd_layout {
+  const fpd_drafter* d = nullptr;
+  HostLayout host;
+  int32_t* dev = nullptr;  // all integer tables
+  void* wg = nullptr;      // gathered legal W_lm rows [n_set_ids, H]
+  // device table pointers (into dev)
+  int32_t *pos_set, *set_offsets, *set_ids, *partner, *field_w, *row_cols, *set_pos;
+  std::vector<int32_t> set_pos_off;  // [n_sets + 2]: positions of set s, then free positions
+  std::vector<int32_t> off_col;      // [n_sets]
+};
+
+namespace {
+
+// ---- workspace plans --------------------------------------------------------------
+struct DraftWs {
+  size_t h, a, q, kb, vbt, o, u, partial, attn, total;
+  size_t partial_bytes, attn_bytes;
+};
+
+size_t gemm_partial_bytes(int dt, int M, int ncols, int K, int nw, bool paired) {
+  if (dt != FPD_DTYPE_BF16) return 0;
+  return plan_gemm_bf16(M, ncols, K, nw, paired).partial_floats * sizeof(float);
+}
+
+DraftWs plan_draft(const fpd_drafter& d, int B, int L, int C) {
+  const fpd_config& c = d.cfg;
+  const size_t e = d.esz, M = (size_t)B * L, H = c.hidden, dh = c.head_dim;
+  const int Lp = round8(L);
+  DraftWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  w.h = take(M * H * 4);
+  w.a = take(M * H * e);
+  w.q = take((size_t)B * c.n_q * L * dh * e);
+  w.kb = take((size_t)B * c.n_kv * L * dh * e);
+  w.vbt = take((size_t)B * c.n_kv * dh * Lp * e);
+  w.o = take(M * c.n_q * dh * e);
+  w.u = take(M * (size_t)c.inter * e);
+  const int dt = c.dtype, m = (int)M, qd = c.n_q * c.head_dim;
+  size_t pb = 0;
+  pb = std::max(pb, gemm_partial_bytes(dt, m, (c.n_q + 2 * c.n_kv) * c.head_dim / 2, c.hidden,
+                                       (c.n_q + 2 * c.n_kv) * c.head_dim, true));
+  pb = std::max(pb, gemm_partial_bytes(dt, m, c.hidden, qd, c.hidden, false));
+  pb = std::max(pb, gemm_partial_bytes(dt, m, c.inter, c.hidden, 2 * c.inter, true));
+  pb = std::max(pb, gemm_partial_bytes(dt, m, c.hidden, c.inter, c.hidden, false));
+  w.partial_bytes = pb;
+  w.partial = take(pb);
+  w.attn_bytes = attention_scratch_bytes(dt, B, L, C, c.n_q, c.n_kv, c.head_dim);
+  w.attn = take(w.attn_bytes);
+  w.total = off;
+  return w;
+}
+
+struct FuseWs {
+  size_t x, z, zn, partial, total, partial_bytes;
+};
+
+FuseWs plan_fuse(const fpd_drafter& d, int B, int C) {
+  const fpd_config& c = d.cfg;
+  const size_t e = d.esz, M = (size_t)B * C, H = c.hidden;
+  FuseWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  w.x = take(c.n_fused > 1 ? M * c.n_fused * H * e : 0);
+  w.z = take(M * H * 4);
+  w.zn = take(M * H * e);
+  size_t pb = gemm_partial_bytes(c.dtype, (int)M, c.hidden, c.n_fused * c.hidden, c.hidden, false);
+  pb = std::max(pb, gemm_partial_bytes(c.dtype, (int)M, c.n_kv * c.head_dim, c.hidden,
+                                       2 * c.n_kv * c.head_dim, true));
+  w.partial_bytes = pb;
+  w.partial = take(pb);
+  w.total = off;
+  return w;
+}
+
+struct HeadWs {
+  size_t pval, pcol, offv, total;
+};
+
+HeadWs plan_head(int B, int L, int max_chunks) {
+  const size_t rows = (size_t)B * (L - 1);
+  HeadWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  w.pval = take(rows * max_chunks * 4);
+  w.pcol = take(rows * max_chunks * 4);
+  w.offv = take(rows * 4);
+  w.total = off;
+  return w;
+}
+
+int32_t check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return FPD_OK;
+  if (!ws) return fail(FPD_E_ARG, "workspace is null");
+  if (ws_bytes < need)
+    return fail(FPD_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                     std::to_string(need));
+  return FPD_OK;
+}
+
+char* wsp(void* ws, size_t off) { return (char*)ws + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fpd_status_string(int32_t s) {
+  switch (s) {
+    case FPD_OK: return "ok";
+    case FPD_E_ARG: return "invalid argument";
+    case FPD_E_SHAPE: return "inconsistent shape";
+    case FPD_E_DTYPE: return "unknown dtype";
+    case FPD_E_SCHEMA: return "invalid schema";
+    case FPD_E_WORKSPACE: return "workspace too small";
+    case FPD_E_UNSUPPORTED: return "unsupported shape";
+    case FPD_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fpd_last_error(void) { return g_err.c_str(); }
+
+int32_t fpd_drafter_create(const fpd_config* cfg, const fpd_weights* w, fpd_drafter** out) {
+  if (!cfg || !w || !out) return fail(FPD_E_ARG, "null argument");
+  *out = nullptr;
+  const fpd_config& c = *cfg;
+  if (c.dtype != FPD_DTYPE_F32 && c.dtype != FPD_DTYPE_BF16) return fail(FPD_E_DTYPE, "unknown dtype");
+  if (c.hidden <= 0 || c.n_q <= 0 || c.n_kv <= 0 || c.head_dim <= 0 || c.n_layers <= 0 || c.inter <= 0 ||
+      c.vocab <= 0 || c.n_fused <= 0)
+    return fail(FPD_E_SHAPE, "every size must be positive");
+  if (c.n_q % c.n_kv != 0) return fail(FPD_E_SHAPE, "n_q must be a multiple of n_kv");
+  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return fail(FPD_E_ARG, "rms_eps >= 0 and rope_theta > 0 required");
+  if (c.hidden % 64 || c.inter % 64 || (c.n_q * c.head_dim) % 64)
+    return fail(FPD_E_UNSUPPORTED, "hidden, inter and n_q*head_dim must be multiples of 64");
+  if (c.dtype == FPD_DTYPE_BF16 && c.head_dim != 128)
+    return fail(FPD_E_UNSUPPORTED, "bf16 drafters need head_dim 128");
+  if (c.dtype == FPD_DTYPE_F32 && c.head_dim != 64 && c.head_dim != 128)
+    return fail(FPD_E_UNSUPPORTED, "f32 drafters need head_dim 64 or 128");
+  if (!w->w_fc || !w->g_fc || !w->embed || !w->w_lm || !w->g_final || !w->layers)
+    return fail(FPD_E_ARG, "null weight pointer");
+  for (int i = 0; i < c.n_layers; ++i) {
+    const fpd_layer_weights& l = w->layers[i];
+    if (!l.g_attn || !l.w_qkv || !l.w_o || !l.g_mlp || !l.w_gu || !l.w_d)
+      return fail(FPD_E_ARG, "null weight pointer in layer " + std::to_string(i));
+  }
+  fpd_drafter* d = new fpd_drafter;
+  d->cfg = c;
+  d->w = *w;
+  d->layers.assign(w->layers, w->layers + c.n_layers);
+  d->w.layers = d->layers.data();
+  d->esz = c.dtype == FPD_DTYPE_BF16 ? 2 : 4;
+  std::memset(&d->tab, 0, sizeof(d->tab));
+  const int half = c.head_dim / 2;
+  for (int i = 0; i < half; ++i)
+    d->tab.inv_freq[i] = (float)std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
+  *out = d;
+  return FPD_OK;
+}
+
+int32_t fpd_drafter_destroy(fpd_drafter* d) {
+  delete d;
+  return FPD_OK;
+}
+
+static int32_t copy_sizes_and_tables(const HostLayout& h, fpd_layout_sizes* sizes, int32_t* pos_set,
+                                     int32_t* set_offsets, int32_t* set_ids, int32_t* pairs,
+                                     int32_t* fields) {
+  if (sizes) {
+    sizes->L = h.L;
+    sizes->n_sets = h.n_sets();
+    sizes->n_set_ids = (int32_t)h.set_ids.size();
+    sizes->n_pairs = (int32_t)h.pairs.size() / 2;
+    sizes->n_fields = (int32_t)h.fields.size() / 2;
+    sizes->width = h.width();
+  }
+  auto cp = [](int32_t* dst, const std::vector<int32_t>& v) {
+    if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(int32_t));
+  };
+  cp(pos_set, h.pos_set);
+  cp(set_offsets, h.set_offsets);
+  cp(set_ids, h.set_ids);
+  cp(pairs, h.pairs);
+  cp(fields, h.fields);
+  return FPD_OK;
+}
+
+int32_t fpd_schema_expand(const fpd_schema* s, int32_t vocab, fpd_layout_sizes* sizes, int32_t* pos_set,
+                          int32_t* set_offsets, int32_t* set_ids, int32_t* pairs, int32_t* fields) {
+  if (!s) return fail(FPD_E_ARG, "null schema");
+  HostLayout h;
+  std::string err;
+  const int32_t st = expand_schema(*s, vocab, &h, &err);
+  if (st != FPD_OK) return fail(st, err);
+  return copy_sizes_and_tables(h, sizes, pos_set, set_offsets, set_ids, pairs, fields);
+}
+
+int32_t fpd_layout_create(const fpd_drafter* d, const fpd_schema* s, fpd_layout** out, int32_t* L_out) {
+  if (!d || !s || !out) return fail(FPD_E_ARG, "null argument");
+  *out = nullptr;
+  fpd_layout* lay = new fpd_layout;
+  lay->d = d;
+  std::string err;
+  int32_t st = expand_schema(*s, d->cfg.vocab, &lay->host, &err);
+  if (st != FPD_OK) {
+    delete lay;
+    return fail(st, err);
+  }
+  const HostLayout& h = lay->host;
+  const int L = h.L, ns = h.n_sets();
+  if (ns > kMaxHeadSets) {
+    delete lay;
+    return fail(FPD_E_UNSUPPORTED, "layouts with more than 32 legal sets are not supported");
+  }
+  // derived tables
+  std::vector<int32_t> partner(L, -1), field_w(L, 0), row_cols(L, 0), set_pos;
+  for (size_t i = 0; i < h.pairs.size(); i += 2) {
+    partner[h.pairs[i]] = h.pairs[i + 1];
+    partner[h.pairs[i + 1]] = -2;
+  }
+  for (size_t i = 0; i < h.fields.size(); i += 2) field_w[h.fields[i]] = h.fields[i + 1];
+  for (int p = 1; p < L; ++p)
+    row_cols[p] = h.pos_set[p] == -1 ? h.vocab : h.set_offsets[h.pos_set[p] + 1] - h.set_offsets[h.pos_set[p]];
+  lay->set_pos_off.assign(ns + 2, 0);
+  for (int s2 = 0; s2 <= ns; ++s2) {
+    lay->set_pos_off[s2] = (int32_t)set_pos.size();
+    const int want = s2 < ns ? s2 : -1;
+    for (int p = 1; p < L; ++p)
+      if (h.pos_set[p] == want) set_pos.push_back(p);
+  }
+  lay->set_pos_off[ns + 1] = (int32_t)set_pos.size();
+  lay->off_col.assign(ns, -1);
+  for (int s2 = 0; s2 < ns; ++s2)
+    for (int i = h.set_offsets[s2]; i < h.set_offsets[s2 + 1]; ++i)
+      if (h.off_id >= 0 && h.set_ids[i] == h.off_id) lay->off_col[s2] = i - h.set_offsets[s2];
+
+  std::vector<int32_t> all;
+  auto put = [&](const std::vector<int32_t>& v) {
+    const size_t o = all.size();
+    all.insert(all.end(), v.begin(), v.end());
+    all.push_back(0);  // keeps every table non-empty
+    return o;
+  };
+  const size_t o_pos = put(h.pos_set), o_off = put(h.set_offsets), o_ids = put(h.set_ids),
+               o_par = put(partner), o_fw = put(field_w), o_rc = put(row_cols), o_sp = put(set_pos);
+  hipError_t e = hipMalloc((void**)&lay->dev, all.size() * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemcpy(lay->dev, all.data(), all.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  const size_t nid = h.set_ids.size(), H = d->cfg.hidden;
+  if (e == hipSuccess && nid > 0) e = hipMalloc(&lay->wg, nid * H * d->esz);
+  if (e == hipSuccess) {
+    lay->pos_set = lay->dev + o_pos;
+    lay->set_offsets = lay->dev + o_off;
+    lay->set_ids = lay->dev + o_ids;
+    lay->partner = lay->dev + o_par;
+    lay->field_w = lay->dev + o_fw;
+    lay->row_cols = lay->dev + o_rc;
+    lay->set_pos = lay->dev + o_sp;
+    if (nid > 0) e = gather_rows(d->cfg.dtype, d->w.w_lm, (int)H, lay->set_ids, (int)nid, lay->wg, nullptr);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    fpd_layout_destroy(lay);
+    return fail(FPD_E_HIP, std::string("layout upload: ") + hipGetErrorString(e));
+  }
+  if (L_out) *L_out = L;
+  *out = lay;
+  return FPD_OK;
+}
+
+int32_t fpd_layout_destroy(fpd_layout* lay) {
+  if (!lay) return FPD_OK;
+  if (lay->dev) (void)hipFree(lay->dev);
+  if (lay->wg) (void)hipFree(lay->wg);
+  delete lay;
+  return FPD_OK;
+}
+
+int32_t fpd_layout_masks(const fpd_layout* lay, fpd_layout_sizes* sizes, int32_t* pos_set,
+                         int32_t* set_offsets, int32_t* set_ids, int32_t* pairs, int32_t* fields) {
+  if (!lay) return fail(FPD_E_ARG, "null layout");
+  return copy_sizes_and_tables(lay->host, sizes, pos_set, set_offsets, set_ids, pairs, fields);
+}
+
+int32_t fpd_workspace_size(const fpd_drafter* d, int32_t B, int32_t C, int32_t L, size_t* bytes) {
+  if (!d || !bytes) return fail(FPD_E_ARG, "null argument");
+  if (B < 1 || C < 0 || L < 2) return fail(FPD_E_SHAPE, "need B >= 1, C >= 0, L >= 2");
+  const int chunk = head_chunk_cols(d->cfg.dtype);
+  const int worst = (d->cfg.vocab + chunk - 1) / chunk;
+  size_t need = plan_draft(*d, B, L, C).total;
+  if (C > 0) need = std::max(need, plan_fuse(*d, B, C).total);
+  need = std::max(need, plan_head(B, L, worst).total);
+  *bytes = need;
+  return FPD_OK;
+}
+
+int32_t fpd_fuse_context_kv(const fpd_drafter* d, const void* feats, int32_t B, int32_t C, int32_t pos0,
+                            void* ctx_k, void* ctx_v, int32_t ctx_cap, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
+  if (B < 1 || C < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C >= 1, pos0 >= 0");
+  if (ctx_cap < C || ctx_cap % 8) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
+  const FuseWs w = plan_fuse(*d, B, C);
+  if (int32_t st = check_ws(ws, ws_bytes, w.total)) return st;
+  const fpd_config& c = d->cfg;
+  const int dt = c.dtype, H = c.hidden, M = B * C, dh = c.head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  const void* X = feats;
+  if (c.n_fused > 1) {
+    FPD_TRY_HIP(concat_features(dt, feats, B, c.n_fused, C, H, wsp(ws, w.x), s));
+    X = wsp(ws, w.x);
+  }
+  float* Z = (float*)wsp(ws, w.z);
+  float* part = (float*)wsp(ws, w.partial);
+  FPD_TRY_HIP(gemm_store_f32(dt, X, c.n_fused * H, M, c.n_fused * H, d->w.w_fc, H, Z, H, part,
+                             w.partial_bytes, s, "gemm_fc"));
+  void* Zn = wsp(ws, w.zn);
+  FPD_TRY_HIP(rmsnorm_rows(dt, Z, H, M, M, 0, 0, d->w.g_fc, c.rms_eps, Zn, s));
+  const size_t per_layer = (size_t)B * c.n_kv * ctx_cap * dh * d->esz;
+  for (int li = 0; li < c.n_layers; ++li) {
+    CtxOut o{};
+    o.k = (char*)ctx_k + li * per_layer;
+    o.vt = (char*)ctx_v + li * per_layer;
+    o.C = C, o.cap = ctx_cap, o.nkv = c.n_kv, o.d = dh, o.pos0 = pos0, o.rope = c.use_rope;
+    o.tab = d->tab;
+    const char* wkv = (const char*)d->layers[li].w_qkv + (size_t)c.n_q * dh * H * d->esz;
+    FPD_TRY_HIP(gemm_ctx_kv(dt, Zn, M, H, wkv, o, part, w.partial_bytes, s));
+  }
+  return FPD_OK;
+}
+
+int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L, const void* ctx_k,
+                        const void* ctx_v, int32_t C, int32_t ctx_cap, int32_t block_pos, void* hidden_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!d || !tokens || !hidden_out) return fail(FPD_E_ARG, "null argument");
+  if (B < 1 || L < 2 || C < 0 || block_pos < 0) return fail(FPD_E_SHAPE, "need B >= 1, L >= 2, C >= 0, block_pos >= 0");
+  if (C > 0 && (!ctx_k || !ctx_v)) return fail(FPD_E_ARG, "null context");
+  if (C > 0 && (ctx_cap < C || ctx_cap % 8)) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
+  const DraftWs w = plan_draft(*d, B, L, C);
+  if (int32_t st = check_ws(ws, ws_bytes, w.total)) return st;
+  const fpd_config& c = d->cfg;
+  const int dt = c.dtype, H = c.hidden, M = B * L, dh = c.head_dim, qd = c.n_q * dh;
+  hipStream_t s = (hipStream_t)stream;
+  float* h = (float*)wsp(ws, w.h);
+  void* a = wsp(ws, w.a);
+  float* part = (float*)wsp(ws, w.partial);
+  FPD_TRY_HIP(embed_gather(dt, tokens, M, d->w.embed, H, c.vocab, h, s));
+  const size_t ctx_layer = (size_t)B * c.n_kv * (size_t)ctx_cap * dh * d->esz;
+  for (int li = 0; li < c.n_layers; ++li) {
+    const fpd_layer_weights& lw = d->layers[li];
+    FPD_TRY_HIP(rmsnorm_rows(dt, h, H, M, M, 0, 0, lw.g_attn, c.rms_eps, a, s));
+    QkvOut qo{};
+    qo.q = wsp(ws, w.q), qo.k = wsp(ws, w.kb), qo.vt = wsp(ws, w.vbt);
+    qo.L = L, qo.Lp = round8(L), qo.nq = c.n_q, qo.nkv = c.n_kv, qo.d = dh, qo.pos0 = block_pos;
+    qo.rope = c.use_rope, qo.tab = d->tab;
+    FPD_TRY_HIP(gemm_qkv(dt, a, M, H, lw.w_qkv, qo, part, w.partial_bytes, s));
+    AttnArgs at{};
+    at.q = qo.q, at.kb = qo.k, at.vbt = qo.vt;
+    at.ck = C > 0 ? (const char*)ctx_k + li * ctx_layer : nullptr;
+    at.cvt = C > 0 ? (const char*)ctx_v + li * ctx_layer : nullptr;
+    at.o = wsp(ws, w.o);
+    at.B = B, at.L = L, at.Lp = qo.Lp, at.C = C, at.cap = ctx_cap, at.nq = c.n_q, at.nkv = c.n_kv, at.d = dh;
+    at.scale = (float)(1.0 / std::sqrt((double)dh));
+    FPD_TRY_HIP(attention(dt, at, wsp(ws, w.attn), w.attn_bytes, s));
+    FPD_TRY_HIP(gemm_residual(dt, at.o, qd, M, qd, lw.w_o, H, h, H, part, w.partial_bytes, s, "gemm_o"));
+    FPD_TRY_HIP(rmsnorm_rows(dt, h, H, M, M, 0, 0, lw.g_mlp, c.rms_eps, a, s));
+    void* u = wsp(ws, w.u);
+    FPD_TRY_HIP(gemm_swiglu(dt, a, M, H, lw.w_gu, c.inter, u, part, w.partial_bytes, s));
+    FPD_TRY_HIP(gemm_residual(dt, u, c.inter, M, c.inter, lw.w_d, H, h, H, part, w.partial_bytes, s,
+                              "gemm_down"));
+  }
+  FPD_TRY_HIP(rmsnorm_rows(dt, h, H, B * (L - 1), L - 1, L, 1, d->w.g_final, c.rms_eps, hidden_out, s));
+  return FPD_OK;
+}
+
+int32_t fpd_constrained_argmax(const fpd_drafter* d, const fpd_layout* lay, const void* hidden, int32_t B,
+                               int32_t* tokens_out, float* logits_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (!d || !lay || !hidden || !tokens_out) return fail(FPD_E_ARG, "null argument");
+  if (lay->d != d) return fail(FPD_E_ARG, "layout was created for another drafter");
+  if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+  const HostLayout& h = lay->host;
+  const fpd_config& c = d->cfg;
+  const int L = h.L, ns = h.n_sets(), chunk = head_chunk_cols(c.dtype);
+  HeadArgs ha{};
+  ha.hidden = hidden;
+  ha.B = B, ha.L = L, ha.H = c.hidden, ha.width = h.width(), ha.logits = logits_out;
+  ReduceArgs ra{};
+  ra.pos_set = lay->pos_set, ra.partner = lay->partner, ra.B = B, ra.L = L, ra.off_id = h.off_id;
+  ra.n_sets = ns, ra.free_slot = ns;
+  int max_chunks = 1;
+  for (int s2 = 0; s2 <= ns; ++s2) {
+    const int npos = lay->set_pos_off[s2 + 1] - lay->set_pos_off[s2];
+    const int ncols = s2 < ns ? h.set_offsets[s2 + 1] - h.set_offsets[s2] : c.vocab;
+    const int nch = (ncols + chunk - 1) / chunk;
+    ra.set_chunks[s2] = nch;
+    ra.set_offcol[s2] = s2 < ns ? lay->off_col[s2] : -1;
+    ra.set_ids[s2] = s2 < ns ? lay->set_ids + h.set_offsets[s2] : nullptr;
+    if (npos == 0) continue;
+    HeadSet& hs = ha.sets[ha.n_sets++];
+    hs.w = s2 < ns ? (const void*)((const char*)lay->wg + (size_t)h.set_offsets[s2] * c.hidden * d->esz)
+                   : d->w.w_lm;
+    hs.ids = ra.set_ids[s2];
+    hs.pos = lay->set_pos + lay->set_pos_off[s2];
+    hs.n_pos = npos, hs.n_cols = ncols, hs.off_col = ra.set_offcol[s2], hs.n_chunks = nch, hs.part_base = 0;
+    max_chunks = std::max(max_chunks, nch);
+  }
+  const HeadWs w = plan_head(B, L, max_chunks);
+  if (int32_t st = check_ws(ws, ws_bytes, w.total)) return st;
+  ha.max_chunks = ra.max_chunks = max_chunks;
+  ha.pval = (float*)wsp(ws, w.pval), ha.pcol = (int32_t*)wsp(ws, w.pcol), ha.offv = (float*)wsp(ws, w.offv);
+  ra.pval = ha.pval, ra.pcol = ha.pcol, ra.offv = ha.offv, ra.tokens = tokens_out;
+  hipStream_t s = (hipStream_t)stream;
+  FPD_TRY_HIP(lm_head_partials(c.dtype, ha, s));
+  if (logits_out) FPD_TRY_HIP(fill_logits_padding(logits_out, B * (L - 1), ha.width, L - 1, lay->row_cols, s));
+  FPD_TRY_HIP(lm_head_reduce(ra, s));
+  return FPD_OK;
+}
+
+int32_t fpd_validate_primitive(const fpd_layout* lay, const int32_t* tokens, int32_t B, int32_t* k_out,
+                               int32_t* first_invalid_out, void* stream) {
+  if (!lay || !tokens || !k_out || !first_invalid_out) return fail(FPD_E_ARG, "null argument");
+  if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+  const HostLayout& h = lay->host;
+  ValidateArgs a{};
+  a.tokens = tokens, a.pos_set = lay->pos_set, a.set_offsets = lay->set_offsets, a.set_ids = lay->set_ids;
+  a.partner = lay->partner, a.field_w = lay->field_w;
+  a.B = B, a.L = h.L, a.vocab = h.vocab, a.off_id = h.off_id, a.fill_id = h.fill_id, a.digit0_id = h.digit0_id;
+  a.k_out = k_out, a.first_out = first_invalid_out;
+  FPD_TRY_HIP(validate_primitive(a, (hipStream_t)stream));
+  return FPD_OK;
+}
+
+int32_t fpd_verify_prefix(const int32_t* draft, const int32_t* target, int32_t B, int32_t L, int32_t* k_out,
+                          int32_t* next_out, void* stream) {
+  if (!draft || !target || !k_out || !next_out) return fail(FPD_E_ARG, "null argument");
+  if (B < 1 || L < 2) return fail(FPD_E_SHAPE, "need B >= 1 and L >= 2");
+  FPD_TRY_HIP(verify_prefix(draft, target, B, L, k_out, next_out, (hipStream_t)stream));
+  return FPD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Shared device-side definitions for the gfx950 kernels of libfpd.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+namespace fpd {
+
+typedef uint16_t bf16_t;  // raw IEEE bfloat16 bits
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, round-robin workgroup dispatch
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// float -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Element load/store in the storage type, arithmetic in float.
+template <class T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <>
+struct Elem<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Maps a linear block index to a tile index so that consecutive tiles land
+// on the same XCD (blocks are dispatched to XCDs round-robin): the tiles an
+// XCD runs together then share operands through that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = n / kXcds, rem = n % kXcds;
+  const int x = bid % kXcds, local = bid / kXcds;
+  return x * per + (x < rem ? x : rem) + local;
+}
+
+// Argmax order of the masked decode: a NaN beats any number; among equal
+// values (or NaNs) the lower column (= lower token id) wins.
+__device__ __forceinline__ bool arg_better(float v1, int c1, float v2, int c2) {
+  const bool n1 = v1 != v1, n2 = v2 != v2;
+  if (n1 != n2) return n1;
+  if (!n1 && v1 != v2) return v1 > v2;
+  return c1 < c2;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// Rotary embedding constants: inverse frequencies theta^(-2i/d) computed on
+// the host in double precision (d/2 <= 64 entries).
+struct RopeTab {
+  float inv_freq[64];
+};
+
+// Rotates the pair (x_i, x_{i + d/2}) by the angle pos * inv_freq[i].
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, int pos, float inv) {
+  float s, c;
+  sincosf((float)pos * inv, &s, &c);
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x1 * c + x0 * s;
+  x0 = y0;
+  x1 = y1;
+}
+
+}  // namespace fpd

@@ -1,0 +1,128 @@
+// Row-wise kernels of the drafter: embedding gather, RMSNorm, feature
+// concatenation, LM-head row gather.
+#include <algorithm>
+
+#include "../../include/fpd.h"
+#include "kernels.h"
+
+namespace fpd {
+namespace {
+
+// h[m] = E[tok[m]]; an id outside [0, V) embeds as a zero row (never read out of bounds).
+template <class T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int M,
+                                                    const T* __restrict__ E, int H, int V, float* __restrict__ h) {
+  const int m = blockIdx.x;
+  const int t = tok[m];
+  float* dst = h + (size_t)m * H;
+  if (t < 0 || t >= V) {
+    for (int k = threadIdx.x; k < H; k += blockDim.x) dst[k] = 0.f;
+    return;
+  }
+  const T* src = E + (size_t)t * H;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) dst[k] = Elem<T>::ld(src + k);
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  const int nw = blockDim.x >> 6;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// One workgroup per output row: y = x / sqrt(mean(x^2) + eps) * g.
+template <class T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, int per,
+                                                      int in_stride, int in_off, const T* __restrict__ g,
+                                                      float eps, T* __restrict__ y) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const float* src = x + ((size_t)(r / per) * in_stride + in_off + r % per) * H;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) {
+    const float v = src[k];
+    ss += v * v;
+  }
+  const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)H + eps);
+  T* dst = y + (size_t)r * H;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) Elem<T>::st(dst + k, src[k] * inv * Elem<T>::ld(g + k));
+}
+
+// X[b*C + c, t*H + k] = feats[b, t, c, k], copied in 16-byte chunks.
+__global__ __launch_bounds__(256) void concat_kernel(const u32x4_t* __restrict__ f, int B, int nt, int C,
+                                                     int Hc, u32x4_t* __restrict__ X) {
+  const size_t n = (size_t)B * nt * C * Hc;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+    const int kc = (int)(e % Hc);
+    size_t r = e / Hc;
+    const int c = (int)(r % C);
+    r /= C;
+    const int t = (int)(r % nt);
+    const int b = (int)(r / nt);
+    X[(((size_t)b * C + c) * nt + t) * Hc + kc] = f[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restrict__ W, int Hc,
+                                                          const int32_t* __restrict__ ids, int n,
+                                                          u32x4_t* __restrict__ out) {
+  const int i = blockIdx.x;
+  if (i >= n) return;
+  const u32x4_t* src = W + (size_t)ids[i] * Hc;
+  for (int k = threadIdx.x; k < Hc; k += blockDim.x) out[(size_t)i * Hc + k] = src[k];
+}
+
+}  // namespace
+
+hipError_t embed_gather(int dt, const int32_t* tokens, int M, const void* E, int H, int V, float* h,
+                        hipStream_t st) {
+  ProfScope prof("embed", st);
+  if (M == 0) return hipSuccess;
+  if (dt == FPD_DTYPE_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st, tokens, M, (const bf16_t*)E, H, V, h);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, tokens, M, (const float*)E, H, V, h);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_rows(int dt, const float* x, int H, int rows, int per, int in_stride, int in_off,
+                        const void* g, float eps, void* y, hipStream_t st) {
+  ProfScope prof("rmsnorm", st);
+  if (rows == 0) return hipSuccess;
+  if (dt == FPD_DTYPE_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, x, H, per, in_stride, in_off,
+                       (const bf16_t*)g, eps, (bf16_t*)y);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, x, H, per, in_stride, in_off,
+                       (const float*)g, eps, (float*)y);
+  return hipGetLastError();
+}
+
+hipError_t concat_features(int dt, const void* feats, int B, int nt, int C, int H, void* X, hipStream_t st) {
+  ProfScope prof("concat", st);
+  const int esz = dt == FPD_DTYPE_BF16 ? 2 : 4;
+  const int Hc = H * esz / 16;
+  const size_t n = (size_t)B * nt * C * Hc;
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(concat_kernel, dim3(grid), dim3(256), 0, st, (const u32x4_t*)feats, B, nt, C, Hc,
+                     (u32x4_t*)X);
+  return hipGetLastError();
+}
+
+hipError_t gather_rows(int dt, const void* W, int H, const int32_t* ids, int n, void* out, hipStream_t st) {
+  ProfScope prof("gather_rows", st);
+  if (n == 0) return hipSuccess;
+  const int esz = dt == FPD_DTYPE_BF16 ? 2 : 4;
+  const int Hc = H * esz / 16;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(256), 0, st, (const u32x4_t*)W, Hc, ids, n,
+                     (u32x4_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace fpd

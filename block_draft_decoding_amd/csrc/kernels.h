@@ -1,0 +1,153 @@
+// Host-side launchers of the gfx950 kernels (internal to libfpd).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "common.h"
+
+namespace fpd {
+
+// Brackets the kernel launches of its lifetime with HIP events on `st` when
+// per-launch timing is enabled (fpd_profile_enable); otherwise a no-op.
+class ProfScope {
+ public:
+  ProfScope(const char* tag, hipStream_t st);
+  ~ProfScope();
+
+ private:
+  hipStream_t st_;
+  int idx_;
+};
+
+// ---- GEMM planning (shared by workspace sizing and launches) --------------
+struct GemmPlan {
+  int bm = 128;       // rows per workgroup tile
+  int m_tiles = 1, n_tiles = 1, splits = 1;
+  size_t partial_floats = 0;  // split-K scratch (splits * M * N_w floats) when splits > 1
+};
+// M rows, ncols logical output columns (pairs for paired epilogues), K depth,
+// nw = W rows covered (partial row length), paired = two W rows per column.
+GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired);
+
+// ---- Y = A W^T with epilogues --------------------------------------------
+// A [M, K] row-major (lda), W [.., K] row-major (ldw = K).  dt: FPD_DTYPE_*.
+// `partial`/`partial_bytes`: split-K scratch from the workspace.
+
+// out[m, n] = Y (float).  N outputs.
+hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const void* W, int N,
+                          float* out, int ldo, float* partial, size_t partial_bytes, hipStream_t st,
+                          const char* tag);
+
+// h[m, n] += Y (float residual).
+hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const void* W, int N,
+                         float* h, int ldh, float* partial, size_t partial_bytes, hipStream_t st,
+                         const char* tag);
+
+// Fused QKV projection of block rows m = b * L + l: Q [B, nq, L, d],
+// K [B, nkv, L, d] (RoPE at pos0 + l), Vt [B, nkv, d, Lp] (transposed).
+struct QkvOut {
+  void *q, *k, *vt;
+  int L, Lp, nq, nkv, d, pos0, rope;
+  RopeTab tab;
+};
+hipError_t gemm_qkv(int dt, const void* A, int M, int K, const void* Wqkv, const QkvOut& o,
+                    float* partial, size_t partial_bytes, hipStream_t st);
+
+// Context K/V of one drafter layer from the fused features, rows m = b * C + c:
+// ctx_k [B, nkv, cap, d] (RoPE at pos0 + c), ctx_vt [B, nkv, d, cap].
+struct CtxOut {
+  void *k, *vt;
+  int C, cap, nkv, d, pos0, rope;
+  RopeTab tab;
+};
+hipError_t gemm_ctx_kv(int dt, const void* Zn, int M, int K, const void* Wkv, const CtxOut& o,
+                       float* partial, size_t partial_bytes, hipStream_t st);
+
+// u[m, i] = silu(A Wg^T)[m, i] * (A Wu^T)[m, i], W = [gate rows; up rows] ([2I, K]).
+hipError_t gemm_swiglu(int dt, const void* A, int M, int K, const void* Wgu, int I, void* u,
+                       float* partial, size_t partial_bytes, hipStream_t st);
+
+// ---- elementwise ------------------------------------------------------------
+hipError_t embed_gather(int dt, const int32_t* tokens, int M, const void* E, int H, int V, float* h,
+                        hipStream_t st);
+// y[r] = RMSNorm(x[row(r)]) * g stored in dt, with row(r) = (r / per) * in_stride + in_off + r % per.
+hipError_t rmsnorm_rows(int dt, const float* x, int H, int rows, int per, int in_stride, int in_off,
+                        const void* g, float eps, void* y, hipStream_t st);
+// X[b * C + c, t * H + k] = feats[b, t, c, k]
+hipError_t concat_features(int dt, const void* feats, int B, int nt, int C, int H, void* X,
+                           hipStream_t st);
+
+// ---- attention ----------------------------------------------------------------
+struct AttnArgs {
+  const void* q;      // [B, nq, L, d]
+  const void* kb;     // [B, nkv, L, d]
+  const void* vbt;    // [B, nkv, d, Lp]
+  const void* ck;     // [B, nkv, cap, d]  (this layer)
+  const void* cvt;    // [B, nkv, d, cap]
+  void* o;            // [B, L, nq * d]
+  int B, L, Lp, C, cap, nq, nkv, d;
+  float scale;
+};
+size_t attention_scratch_bytes(int dt, int B, int L, int C, int nq, int nkv, int d);
+hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_bytes, hipStream_t st);
+
+// ---- constrained LM head -------------------------------------------------------
+constexpr int kMaxHeadSets = 32;
+struct HeadSet {
+  const void* w;           // legal rows [n_cols, H] (gathered), or W_lm for free positions
+  const int32_t* ids;      // ascending ids [n_cols], nullptr = identity (free)
+  const int32_t* pos;      // block positions (1..L-1) that use this set
+  int n_pos, n_cols, off_col;  // off_col: column of the OFF id, -1 if none
+  int n_chunks, part_base;     // column chunks; first chunk slot of this set in a row's partials
+};
+struct HeadArgs {
+  const void* hidden;      // [B, L-1, H]
+  int B, L, H, width, n_sets, max_chunks;
+  HeadSet sets[kMaxHeadSets];
+  float* logits;           // nullable [B, L-1, width]
+  float* pval;             // [B*(L-1), max_chunks]
+  int32_t* pcol;           // [B*(L-1), max_chunks]
+  float* offv;             // [B*(L-1)]
+};
+int head_chunk_cols(int dt);
+hipError_t lm_head_partials(int dt, const HeadArgs& a, hipStream_t st);
+// Combines the chunk partials into tokens; applies the OFF pairing rule.
+struct ReduceArgs {
+  const int32_t* pos_set;   // [L]
+  const int32_t* partner;   // [L]: partner of a pair's first position, -2 second, -1 none
+  int B, L, off_id, max_chunks, n_sets;
+  int set_chunks[kMaxHeadSets + 1];
+  int set_offcol[kMaxHeadSets + 1];
+  const int32_t* set_ids[kMaxHeadSets + 1];   // nullptr = identity
+  int free_slot;            // index used for free positions (-1 if none)
+  const float* pval;
+  const int32_t* pcol;
+  const float* offv;
+  int32_t* tokens;
+};
+hipError_t lm_head_reduce(const ReduceArgs& a, hipStream_t st);
+// logits[r, c] = -inf for c >= row_cols[r % P + 1] (P = L - 1).
+hipError_t fill_logits_padding(float* logits, int rows, int width, int P, const int32_t* row_cols,
+                               hipStream_t st);
+
+// ---- acceptance -------------------------------------------------------------------
+struct ValidateArgs {
+  const int32_t* tokens;     // [B, L-1]
+  const int32_t* pos_set;    // [L]
+  const int32_t* set_offsets;
+  const int32_t* set_ids;
+  const int32_t* partner;    // [L]
+  const int32_t* field_w;    // [L]: width at a field's first digit position, else 0
+  int B, L, vocab, off_id, fill_id, digit0_id;
+  int32_t* k_out;
+  int32_t* first_out;
+};
+hipError_t validate_primitive(const ValidateArgs& a, hipStream_t st);
+hipError_t verify_prefix(const int32_t* draft, const int32_t* target, int B, int L, int32_t* k_out,
+                         int32_t* next_out, hipStream_t st);
+hipError_t gather_rows(int dt, const void* W, int H, const int32_t* ids, int n, void* out,
+                       hipStream_t st);
+
+}  // namespace fpd

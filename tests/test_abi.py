@@ -1,0 +1,156 @@
+"""Host-only checks of the C ABI: the library loads and exports every symbol
+the header declares; the layout builder agrees bit-exactly with the oracle's
+own construction; argument errors are reported before any GPU work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_draft_decoding_amd import synth
+from oracle import fpd_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+fpd = pytest.importorskip("block_draft_decoding_amd.fpd", reason="libfpd.so not built")
+
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "fpd.h")).read()
+    names = sorted(set(re.findall(r"\b(fpd_[a-z_]+)\s*\(", header)))
+    assert len(names) >= 14
+    lib = ctypes.CDLL(fpd.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def _small_schemas():
+    V = 4099
+    ids = dict(start_id=4095, mask_id=4098, delim_id=4080, off_id=-1, plus_id=4082, minus_id=4083,
+               digit0_id=4084, fill_id=4094, coord_base=3079, coord_count=1001)
+    out = [
+        (dict(kind="text", block_len=37, **ids), V),
+        (dict(kind="traj2d", n_points=5, **ids), V),
+        (dict(kind="traj2d3d", n_points=7, **{**ids, "off_id": 4081}), V),
+        (dict(kind="traj2d3d", n_points=3, **ids), V),
+        (dict(kind="points3d_text", n_points=4, **ids), V),
+        (dict(kind="custom", block_len=9, sets=[[7, 3, 3, 5], [1], [2, 9, 4]],
+              pos_set=[-2, 0, 1, -1, 2, 0, -1, 1, 2], pairs=[(1, 5)], fields=[], off_id=5,
+              fill_id=-1, digit0_id=-1, coord_base=0, coord_count=0), 16),
+    ]
+    for name, wl in synth.WORKLOADS.items():
+        out.append((wl.schema, wl.shape.vocab))
+    return out
+
+
+@pytest.mark.parametrize("idx", range(11))
+def test_schema_expand_matches_oracle_layout(idx):
+    schema, V = _small_schemas()[idx]
+    got = fpd.fpd_schema_expand(schema, V)
+    lay = O.build_layout(schema, V)
+    offs, ids = lay.csr()
+    assert got["L"] == lay.L
+    assert np.array_equal(got["pos_set"], lay.pos_set)
+    assert np.array_equal(got["set_offsets"], offs)
+    assert np.array_equal(got["set_ids"], ids)
+    assert np.array_equal(got["pairs"], np.asarray(lay.pairs, np.int32).reshape(-1, 2))
+    assert np.array_equal(got["fields"], np.asarray(lay.fields, np.int32).reshape(-1, 2))
+    widths = [len(lay.legal(p)) for p in range(1, lay.L)]
+    assert got["width"] == max(widths)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(kind="traj2d", n_points=0), fpd.FPD_E_SCHEMA),
+    (dict(kind="traj2d", n_points=2, coord_base=4000), fpd.FPD_E_SCHEMA),       # coords past the vocabulary
+    (dict(kind="traj2d3d", n_points=2, off_id=3100), fpd.FPD_E_SCHEMA),         # OFF inside the coordinates
+    (dict(kind="points3d_text", n_points=2, fill_id=4084), fpd.FPD_E_SCHEMA),   # fill equals a digit
+    (dict(kind="text", block_len=1), fpd.FPD_E_SCHEMA),
+    (dict(kind="custom", block_len=3, sets=[[1]], pos_set=[0, 0, 0]), fpd.FPD_E_SCHEMA),
+    (dict(kind="custom", block_len=3, sets=[[]], pos_set=[-2, 0, 0]), fpd.FPD_E_SCHEMA),
+    (dict(kind="custom", block_len=3, sets=[[1, 2]], pos_set=[-2, 0, 0], pairs=[(1, 2)]), fpd.FPD_E_SCHEMA),
+    (dict(kind="custom", block_len=4, sets=[[1]], pos_set=[-2, 0, 0, 0], fields=[(2, 5)], fill_id=3,
+          digit0_id=5), fpd.FPD_E_SCHEMA),
+])
+def test_schema_errors(bad, code):
+    base = dict(start_id=4095, mask_id=4098, delim_id=4080, off_id=-1, plus_id=4082, minus_id=4083,
+                digit0_id=4084, fill_id=4094, coord_base=3079, coord_count=1001, block_len=0, n_points=0)
+    base.update(bad)
+    with pytest.raises(fpd.FpdError) as e:
+        fpd.fpd_schema_expand(base, 4099)
+    assert e.value.status == code
+    assert fpd.fpd_last_error()
+
+
+def _cfg(**kw):
+    c = fpd.make_config(synth.DRAFTER_TINY)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _fake_weights(n_layers):
+    # non-null host addresses: creation only records pointers, it never dereferences them
+    lw = (fpd.fpd_layer_weights * n_layers)()
+    for i in range(n_layers):
+        for k in ("g_attn", "w_qkv", "w_o", "g_mlp", "w_gu", "w_d"):
+            setattr(lw[i], k, 4096)
+    w = fpd.fpd_weights(4096, 4096, 4096, 4096, 4096, lw)
+    return w, lw
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=7), fpd.FPD_E_DTYPE),
+    (dict(hidden=0), fpd.FPD_E_SHAPE),
+    (dict(n_q=3), fpd.FPD_E_SHAPE),
+    (dict(hidden=100), fpd.FPD_E_UNSUPPORTED),
+    (dict(head_dim=32), fpd.FPD_E_UNSUPPORTED),
+    (dict(dtype=1, head_dim=64), fpd.FPD_E_UNSUPPORTED),
+])
+def test_drafter_create_errors(over, code):
+    c = _cfg(**over)
+    w, keep = _fake_weights(max(1, c.n_layers))
+    h = ctypes.c_void_p()
+    st = fpd._create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h))
+    assert st == code and not h.value
+
+
+def test_hot_calls_reject_bad_arguments_without_gpu_work():
+    c = _cfg()
+    w, keep = _fake_weights(c.n_layers)
+    h = ctypes.c_void_p()
+    assert fpd._create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == fpd.FPD_OK
+    try:
+        n = ctypes.c_size_t()
+        assert fpd._ws_size(h, 1, 64, 16, ctypes.byref(n)) == fpd.FPD_OK and n.value > 0
+        assert fpd._ws_size(h, 0, 64, 16, ctypes.byref(n)) == fpd.FPD_E_SHAPE
+        # null tokens / outputs
+        assert fpd._draft(h, None, 1, 16, None, None, 0, 0, 0, None, None, 0, None) == fpd.FPD_E_ARG
+        # L < 2
+        assert fpd._draft(h, 8, 1, 1, None, None, 0, 0, 0, 8, None, 0, None) == fpd.FPD_E_SHAPE
+        # context capacity below C
+        assert fpd._draft(h, 8, 1, 16, 8, 8, 64, 32, 64, 8, None, 0, None) == fpd.FPD_E_SHAPE
+        # capacity not a multiple of 8
+        assert fpd._fuse(h, 8, 1, 60, 0, 8, 8, 62, None, 0, None) == fpd.FPD_E_SHAPE
+        # workspace too small
+        assert fpd._draft(h, 8, 1, 16, 8, 8, 64, 64, 64, 8, 8, 16, None) == fpd.FPD_E_WORKSPACE
+        assert fpd._argmax(h, None, 8, 1, 8, None, 8, 1 << 20, None) == fpd.FPD_E_ARG
+        assert fpd._verify(8, 8, 1, 1, 8, 8, None) == fpd.FPD_E_SHAPE
+        assert fpd._validate(None, 8, 1, 8, 8, None) == fpd.FPD_E_ARG
+    finally:
+        fpd._destroy(h)
+
+
+def test_workspace_grows_with_the_problem():
+    c = fpd.make_config(synth.DRAFTER_4B)
+    w, keep = _fake_weights(c.n_layers)
+    h = ctypes.c_void_p()
+    assert fpd._create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == fpd.FPD_OK
+    try:
+        sizes = []
+        for (B, C, L) in [(1, 2048, 16), (1, 4096, 385), (8, 4096, 2433)]:
+            n = ctypes.c_size_t()
+            assert fpd._ws_size(h, B, C, L, ctypes.byref(n)) == fpd.FPD_OK
+            sizes.append(n.value)
+        assert sizes[0] < sizes[1] < sizes[2] < (8 << 30)
+    finally:
+        fpd._destroy(h)

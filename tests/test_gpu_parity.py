@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Bit-exact for token ids, masks and accepted lengths;
+floating point within 2e-2 (bf16) / 1e-4 (fp32) relative in the form
+|g - o| <= tol * max(|o|, rms(o)); argmax agreement wherever the oracle's
+top-2 legal-logit gap exceeds 1e-2."""
+import itertools
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from block_draft_decoding_amd import synth
+from oracle import fpd_oracle as O
+from tests.gpu_cases import (GpuCase, check_tokens, legal_rms, oracle_result, progress, rel_close,
+                             small_ids, to_np, top2_gap, workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = synth.DrafterShape(hidden=512, n_q=8, n_kv=2, head_dim=128, n_layers=2, inter=1408, vocab=4099,
+                           n_fused=3, dtype="bf16", weight_std=0.02)
+
+
+def small_workload(kind, B, C, seed, shape=SMALL, **schema_over):
+    ids = small_ids(shape.vocab)
+    schema = dict(kind=kind, **ids)
+    schema.update(schema_over)
+    return synth.Workload(f"small-{kind}", shape, batch=B, ctx=C, schema=schema, seed_index=seed,
+                          off_row_std=0.06 if schema.get("off_id", -1) >= 0 else None)
+
+
+def run_both(wl, n_layers=None, logits=True):
+    inp = synth.make_inputs(wl)
+    g = GpuCase(wl, inp, n_layers=n_layers)
+    g.fuse()
+    g.draft()
+    lg = g.argmax(logits=logits)
+    torch.cuda.synchronize()
+    shape = wl.shape if n_layers is None else replace(wl.shape, n_layers=n_layers)
+    w = inp.weights if n_layers is None else replace(inp.weights, layers=inp.weights.layers[:n_layers])
+    res = O.run_block(O.Model(shape, w), inp.feats, inp.tokens, wl.schema, want_logits=True)
+    return inp, g, lg, res
+
+
+def compare_all(wl, g, lg, res, dtype, name=""):
+    stats = {}
+    if wl.ctx > 0:
+        ck, cv = g.ctx_np()
+        stats["ctx_k"] = rel_close(ck, res["ctx_k"], dtype, "ctx_k")
+        stats["ctx_v"] = rel_close(cv, res["ctx_v"], dtype, "ctx_v")
+    stats["hidden"] = rel_close(to_np(g.hidden), res["hidden"], dtype, "hidden")
+    lay = res["layout"]
+    if lg is not None:
+        stats["logits"] = rel_close(to_np(lg), O.gathered_logits(res["logits"], lay), dtype, "logits")
+    gap = top2_gap(res["logits"], lay)
+    got = g.toks.cpu().numpy()
+    stats["tokens"] = check_tokens(got, res["tokens"], gap, legal_rms(res["logits"], lay), dtype, "tokens")
+    for b in range(got.shape[0]):
+        for p in range(1, lay.L):
+            assert got[b, p - 1] in lay.legal(p)
+    progress(f"[parity {name}] " + ", ".join(
+        f"{k}: row {v[0]:.2e} elem {v[1]:.2e}" for k, v in stats.items() if k != "tokens") +
+        f"; tokens agree/differ(gap>1e-2)/differ(near tie) {stats['tokens']}")
+    return stats
+
+
+@pytest.mark.parametrize("kind,B,C,over", [
+    ("text", 2, 300, dict(block_len=37)),
+    ("traj2d3d", 2, 300, dict(n_points=7, off_id=4099 - 1020 + 1002)),
+    ("points3d_text", 3, 77, dict(n_points=2)),
+    ("traj2d", 1, 0, dict(n_points=1)),
+    ("text", 1, 64, dict(block_len=2)),
+])
+def test_small_bf16_end_to_end(kind, B, C, over):
+    wl = small_workload(kind, B, C, seed=40 + B, **over)
+    inp, g, lg, res = run_both(wl)
+    compare_all(wl, g, lg, res, "bf16", f"small {kind} B={B} C={C}")
+    lay = res["layout"]
+    if kind != "text":
+        k, f = g.validate(torch.from_numpy(res["tokens"]).cuda())
+        ko, fo = O.validate_primitive(res["tokens"], lay)
+        assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
+    if kind == "traj2d3d":
+        n_off = int((res["tokens"] == lay.off_id).sum())
+        progress(f"[pairs] off-frame tokens {n_off} of {res['tokens'].size}")
+
+
+@pytest.mark.parametrize("n_layers", [1, 2, 3])
+def test_per_layer_hidden_parity(n_layers):
+    shape = replace(SMALL, n_layers=3)
+    wl = small_workload("text", 1, 200, seed=50, shape=shape, block_len=21)
+    inp, g, lg, res = run_both(wl, n_layers=n_layers, logits=False)
+    r = rel_close(to_np(g.hidden), res["hidden"], "bf16", f"hidden after {n_layers} layers")
+    progress(f"[layers {n_layers}] hidden row {r[0]:.2e} elem {r[1]:.2e}")
+
+
+def test_tiny_fp32_workload():
+    wl, inp = workload_inputs("tiny")
+    g = GpuCase(wl, inp)
+    g.fuse()
+    g.draft()
+    lg = g.argmax(logits=True)
+    torch.cuda.synchronize()
+    res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
+    compare_all(wl, g, lg, res, "f32", "tiny fp32")
+    k, f = g.validate()
+    ko, fo = O.validate_primitive(g.toks.cpu().numpy(), res["layout"])
+    assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
+    # text verification with every planted prefix length 0..15
+    draft = np.repeat(res["tokens"], 16, axis=0)
+    tgt = synth.plant_targets(draft, np.arange(16), wl.shape.vocab, 3001)
+    kk = torch.empty(16, dtype=torch.int32, device="cuda")
+    nx = torch.empty_like(kk)
+    g.fpd.fpd_verify_prefix(torch.from_numpy(draft).cuda(), torch.from_numpy(tgt).cuda(), kk, nx)
+    ko, no = O.verify_prefix(draft, tgt)
+    assert np.array_equal(kk.cpu().numpy(), np.arange(16)) and np.array_equal(kk.cpu().numpy(), ko)
+    assert np.array_equal(nx.cpu().numpy(), no)
+
+
+def test_rope_shift_invariance_on_gpu():
+    wl, inp = workload_inputs("tiny")
+    g = GpuCase(wl, inp)
+    g.fuse(pos0=0)
+    g.draft()
+    a = to_np(g.hidden)
+    g.fuse(pos0=1000)
+    g.draft(block_pos=wl.ctx + 1000)
+    b = to_np(g.hidden)
+    # fp32 angles at positions ~1000 carry ~1e-4 relative rounding, so the
+    # invariance holds to that level rather than to the 1e-4 parity bound
+    rows = np.linalg.norm(b - a, axis=-1) / np.linalg.norm(a, axis=-1)
+    assert rows.max() < 1e-3, rows.max()
+
+
+def test_zero_lm_head_ties_pick_lowest_ids():
+    wl = small_workload("traj2d3d", 2, 50, seed=61, n_points=3, off_id=4099 - 1020 + 1002)
+    inp = synth.make_inputs(wl)
+    inp.weights.w_lm[...] = 0.0
+    g = GpuCase(wl, inp)
+    g.fuse()
+    g.draft()
+    g.argmax()
+    torch.cuda.synchronize()
+    lay = O.build_layout(wl.schema, wl.shape.vocab)
+    want = np.array([[lay.legal(p)[0] for p in range(1, lay.L)]] * 2, np.int32)
+    assert np.array_equal(g.toks.cpu().numpy(), want)
+
+
+def test_validator_planted_errors_bit_exact():
+    wl = small_workload("points3d_text", 1, 16, seed=62, n_points=6)
+    inp = synth.make_inputs(wl)
+    g = GpuCase(wl, inp)
+    lay = O.build_layout(wl.schema, wl.shape.vocab)
+    sch = wl.schema
+    rng = np.random.default_rng(9)
+    B = 512
+    toks = np.empty((B, lay.L - 1), np.int32)
+    for p in range(1, lay.L):
+        ids = lay.legal(p)
+        toks[:, p - 1] = ids[rng.integers(0, len(ids), size=B)]
+    for (p0, w) in lay.fields:      # well-formed fields: FILL^j DIGIT^(w-j)
+        j = rng.integers(0, w, size=B)
+        for i in range(w):
+            dig = sch["digit0_id"] + rng.integers(0, 10, size=B)
+            toks[:, p0 - 1 + i] = np.where(i < j, sch["fill_id"], dig)
+    # plant errors in half the rows: fill after a digit, foreign ids, out-of-vocabulary ids
+    for b in range(0, B, 2):
+        for _ in range(rng.integers(1, 3)):
+            toks[b, rng.integers(0, lay.L - 1)] = rng.choice([sch["fill_id"], 5, -3, 10 ** 6])
+    k, f = g.validate(torch.from_numpy(toks).cuda())
+    ko, fo = O.validate_primitive(toks, lay)
+    assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
+    assert B // 2 <= int((ko > 0).sum()) < B
+
+
+def test_verify_brute_force_v3_l5():
+    from block_draft_decoding_amd import fpd
+    V, L = 3, 5
+    drafts = np.array(list(itertools.product(range(V), repeat=L - 1)), np.int32)
+    targets = np.array(list(itertools.product(range(V), repeat=L)), np.int32)
+    D = np.ascontiguousarray(np.repeat(drafts, len(targets), axis=0))
+    T = np.ascontiguousarray(np.tile(targets, (len(drafts), 1)))
+    k = torch.empty(D.shape[0], dtype=torch.int32, device="cuda")
+    nx = torch.empty_like(k)
+    fpd.fpd_verify_prefix(torch.from_numpy(D).cuda(), torch.from_numpy(T).cuda(), k, nx)
+    ko, no = O.verify_prefix(D, T)
+    assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(nx.cpu().numpy(), no)
+
+
+def test_layout_masks_on_device_match_oracle():
+    wl, inp = workload_inputs("tiny")
+    g = GpuCase(wl, inp)
+    from block_draft_decoding_amd import fpd
+    for name in ("text", "traj2d", "traj2d3d", "points3d"):
+        w = synth.WORKLOADS[name]
+        small = replace(w, shape=replace(SMALL, vocab=151_936), schema=w.schema)
+        # masks only depend on the schema and the vocabulary
+        m = fpd.fpd_schema_expand(small.schema, 151_936)
+        lay = O.build_layout(small.schema, 151_936)
+        offs, ids = lay.csr()
+        assert np.array_equal(m["pos_set"], lay.pos_set) and np.array_equal(m["set_ids"], ids)
+    m = fpd.fpd_layout_masks(g.lay)
+    lay = O.build_layout(wl.schema, wl.shape.vocab)
+    assert np.array_equal(m["pos_set"], lay.pos_set)
+    assert np.array_equal(m["set_offsets"], lay.csr()[0]) and np.array_equal(m["set_ids"], lay.csr()[1])
+
+
+def test_determinism_bitwise():
+    wl = small_workload("traj2d3d", 1, 300, seed=63, n_points=5, off_id=4099 - 1020 + 1002)
+    inp = synth.make_inputs(wl)
+    g = GpuCase(wl, inp)
+    outs = []
+    for _ in range(2):
+        g.fuse()
+        g.draft()
+        lg = g.argmax(logits=True)
+        torch.cuda.synchronize()
+        outs.append((g.hidden.clone(), g.toks.clone(), lg.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][2], outs[1][2])
+
+
+# ---- full-size workloads ------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["text", "traj2d", "traj2d3d"])
+def test_full_size_workload(name):
+    wl, inp = workload_inputs(name)
+    g = GpuCase(wl, inp)
+    g.fuse()
+    g.draft()
+    lg = g.argmax(logits=True)
+    torch.cuda.synchronize()
+    progress(f"[gpu] {name} done")
+    res = oracle_result(name)
+    compare_all(wl, g, lg, res, "bf16", f"full {name}")
+    lay = res["layout"]
+    if name == "text":
+        B = wl.batch
+        draft = np.repeat(res["tokens"], 16, axis=0)
+        tgt = synth.plant_targets(draft, np.arange(16), wl.shape.vocab, 3002)
+        kk = torch.empty(16, dtype=torch.int32, device="cuda")
+        nx = torch.empty_like(kk)
+        g.fpd.fpd_verify_prefix(torch.from_numpy(draft).cuda(), torch.from_numpy(tgt).cuda(), kk, nx)
+        assert np.array_equal(kk.cpu().numpy(), np.arange(16))
+        assert np.array_equal(nx.cpu().numpy(), tgt[np.arange(16), np.arange(16)])
+    else:
+        k, f = g.validate()
+        ko, fo = O.validate_primitive(g.toks.cpu().numpy(), lay)
+        assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
+        if name == "traj2d3d":
+            n_off = int((g.toks.cpu().numpy() == lay.off_id).sum())
+            progress(f"[pairs] off-frame tokens {n_off} of {g.toks.numel()}")
+
+
+def test_full_size_points3d_sampled():
+    """B=8, L=2433, C=4096: the oracle cannot run the whole block in seconds,
+    so the sampled checks are: the LM head, argmax and validator on the GPU's
+    own hidden states for sampled rows, the context fusion for sampled
+    context rows, and legality of every token."""
+    wl, inp = workload_inputs("points3d")
+    g = GpuCase(wl, inp)
+    g.fuse()
+    g.draft()
+    g.argmax()
+    torch.cuda.synchronize()
+    m = O.Model(wl.shape, inp.weights)
+    lay = O.build_layout(wl.schema, wl.shape.vocab)
+    hid = to_np(g.hidden)
+    assert np.all(np.isfinite(hid))
+    toks = g.toks.cpu().numpy()
+    rng = np.random.default_rng(5)
+    rows = rng.choice(wl.batch * (lay.L - 1), size=48, replace=False)
+    # sampled LM head: logits of the sampled rows from the GPU hidden states
+    H = wl.shape.hidden
+    hs = hid.reshape(-1, H)[rows]
+    lay_rows = [(int(r) // (lay.L - 1), int(r) % (lay.L - 1) + 1) for r in rows]
+    for (b, p), h in zip(lay_rows, hs):
+        ids = lay.legal(p)
+        z = inp.weights.w_lm[ids].astype(np.float64) @ h.astype(np.float64)
+        order = np.argsort(-z, kind="stable")
+        want = ids[order[0]]
+        gap = z[order[0]] - z[order[1]] if len(ids) > 1 else np.inf
+        if gap > 1e-2:
+            assert toks[b, p - 1] == want, (b, p)
+    for b in range(wl.batch):
+        for p in range(1, lay.L):
+            assert toks[b, p - 1] in lay.legal(p)
+    k, f = g.validate()
+    ko, fo = O.validate_primitive(toks, lay)
+    assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
+    # sampled context rows of the fusion
+    ck, cv = g.ctx_np()
+    samp = [(int(b), int(c)) for b, c in zip(rng.integers(0, wl.batch, 16), rng.integers(0, wl.ctx, 16))]
+    for (b, c) in samp:
+        sub = inp.feats[b:b + 1, :, c:c + 1, :]
+        kk, vv = O.fuse_context_kv(m, sub, ctx_pos0=c)
+        rel_close(ck[:, b, c], kk[:, 0, 0], "bf16", f"ctx_k row {b},{c}")
+        rel_close(cv[:, b, c], vv[:, 0, 0], "bf16", f"ctx_v row {b},{c}")
+    progress(f"[full points3d] valid requests {int((ko > 0).sum())} of {wl.batch}")
