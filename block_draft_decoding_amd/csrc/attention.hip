@@ -25,9 +25,8 @@ namespace {
 
 constexpr int KT = 64;          // keys per tile
 constexpr int D = 128;          // head dim of the bf16 path
-constexpr int KLD = D + 8;      // K tile row stride (bf16 elements)
-constexpr int VLD = KT + 8;     // V^T tile row stride
 constexpr int QROWS = 128;      // packed query rows per workgroup (4 waves x 32)
+constexpr float kRescale = 8.0f;  // lazy rescale: keep the running max until it grows by 2^8
 
 struct AttnP {
   const bf16_t *q, *kb, *vbt, *ck, *cvt;
@@ -40,9 +39,15 @@ struct AttnP {
 
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnP p) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * VLD];
+// LDS tiles hold 16-byte chunks without padding; chunk positions are XOR
+// swizzled so the MFMA operand reads (16 rows x 16 bytes per LDS cycle) hit
+// distinct banks.  K tile: 64 keys x 16 chunks; V^T tile: 128 dims x 8 chunks.
+__device__ __forceinline__ int kslot(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+__device__ __forceinline__ int vslot(int d, int c) { return d * 8 + (c ^ ((d >> 1) & 7)); }
+
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
+  __shared__ u32x4_t Ks[2][KT * 16];
+  __shared__ u32x4_t Vs[2][D * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -61,73 +66,64 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnP p) {
   const bf16_t* qbase = p.q + ((size_t)(b * p.nq + j * p.g) * p.L) * D;
   bf16x8_t qf[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (qvalid)
-      qf[kk] = *(const bf16x8_t*)(qbase + (size_t)qrow * D + kk * 16 + lg * 8);
-    else
-      qf[kk] = bf16x8_t{};
-  }
+  for (int kk = 0; kk < D / 16; ++kk)
+    qf[kk] = qvalid ? *(const bf16x8_t*)(qbase + (size_t)qrow * D + kk * 16 + lg * 8) : bf16x8_t{};
 
   const int total = p.ctx_tiles + p.blk_tiles;
   const int t0 = (int)((long)sp * total / p.splits), t1 = (int)((long)(sp + 1) * total / p.splits);
   const size_t bhk = (size_t)b * p.nkv + j;
 
-  // tile source
-  auto src = [&](int t, const bf16_t*& kptr, const bf16_t*& vptr, int& ldv, int& key0, int& count) {
+  struct Src {
+    const bf16_t *k, *v;
+    int ldv, key0, count;
+  };
+  auto src = [&](int t) {
+    Src r;
     if (t < p.ctx_tiles) {
-      key0 = t * KT;
-      count = p.C;
-      kptr = p.ck + bhk * p.cap * D;
-      vptr = p.cvt + bhk * D * p.cap;
-      ldv = p.cap;
+      r.key0 = t * KT, r.count = p.C, r.ldv = p.cap;
+      r.k = p.ck + bhk * p.cap * D;
+      r.v = p.cvt + bhk * D * p.cap;
     } else {
-      key0 = (t - p.ctx_tiles) * KT;
-      count = p.L;
-      kptr = p.kb + bhk * p.L * D;
-      vptr = p.vbt + bhk * D * p.Lp;
-      ldv = p.Lp;
+      r.key0 = (t - p.ctx_tiles) * KT, r.count = p.L, r.ldv = p.Lp;
+      r.k = p.kb + bhk * p.L * D;
+      r.v = p.vbt + bhk * D * p.Lp;
     }
+    return r;
   };
 
+  // staging: thread handles LDS slots tid + i*256 of each tile; the global
+  // chunk it loads is chosen so that the swizzled layout comes out directly
   u32x4_t rk[4], rv[4];
-  int cur_count = 0, cur_key0 = 0;
   auto gload = [&](int t) {
-    const bf16_t *kp, *vp;
-    int ldv, key0, count;
-    src(t, kp, vp, ldv, key0, count);
+    const Src sr = src(t);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int krow = c >> 4, kc = (c & 15) * 8;
-      rk[i] = (key0 + krow < count) ? *(const u32x4_t*)(kp + (size_t)(key0 + krow) * D + kc)
-                                    : u32x4_t{0, 0, 0, 0};
-      const int drow = c >> 3, vc = (c & 7) * 8;
-      const int kabs = key0 + vc;
-      if (kabs < count) {
-        u32x4_t v = *(const u32x4_t*)(vp + (size_t)drow * ldv + kabs);
-        const int nvalid = count - kabs;  // keys beyond the valid count become exact zeros
+      const int sl = tid + i * 256;
+      const int kr = sl >> 4, kc = (sl & 15) ^ (kr & 15);
+      rk[i] = (sr.key0 + kr < sr.count) ? *(const u32x4_t*)(sr.k + (size_t)(sr.key0 + kr) * D + kc * 8)
+                                        : u32x4_t{0, 0, 0, 0};
+      const int dr = sl >> 3, vc = (sl & 7) ^ ((dr >> 1) & 7);
+      const int kabs = sr.key0 + vc * 8;
+      u32x4_t v = u32x4_t{0, 0, 0, 0};
+      if (kabs < sr.count) {
+        v = *(const u32x4_t*)(sr.v + (size_t)dr * sr.ldv + kabs);
+        const int nvalid = sr.count - kabs;  // keys past the valid count become exact zeros
         if (nvalid < 8) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int k0e = 2 * e;
-            uint32_t w = v[e];
-            if (k0e >= nvalid) w = 0;
-            else if (k0e + 1 >= nvalid) w &= 0xffffu;
-            v[e] = w;
+            if (2 * e >= nvalid) v[e] = 0;
+            else if (2 * e + 1 >= nvalid) v[e] &= 0xffffu;
           }
         }
-        rv[i] = v;
-      } else {
-        rv[i] = u32x4_t{0, 0, 0, 0};
       }
+      rv[i] = v;
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      *(u32x4_t*)&Ks[buf][(c >> 4) * KLD + (c & 15) * 8] = rk[i];
-      *(u32x4_t*)&Vs[buf][(c >> 3) * VLD + (c & 7) * 8] = rv[i];
+      Ks[buf][tid + i * 256] = rk[i];
+      Vs[buf][tid + i * 256] = rv[i];
     }
   };
 
@@ -137,6 +133,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnP p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const int krow0 = swap23(lq);
 
   if (t0 < t1) {
     gload(t0);
@@ -145,68 +142,74 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnP p) {
   }
   for (int t = t0; t < t1; ++t) {
     const int cur = (t - t0) & 1;
-    {
-      const bf16_t *kp, *vp;
-      int ldv;
-      src(t, kp, vp, ldv, cur_key0, cur_count);
-    }
+    const Src sr = src(t);
     if (t + 1 < t1) gload(t + 1);
     if (wave_active) {
+      const bf16x8_t* Kb = (const bf16x8_t*)Ks[cur];
+      const bf16x8_t* Vb = (const bf16x8_t*)Vs[cur];
       f32x16_t s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const int krow = kb * 32 + swap23(lq);
+        const int krow = kb * 32 + krow0;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8_t kf = *(const bf16x8_t*)&Ks[cur][krow * KLD + kk * 16 + lg * 8];
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
-        }
+        for (int kk = 0; kk < D / 16; ++kk)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[kslot(krow, kk * 2 + lg)], qf[kk], s[kb], 0, 0, 0);
       }
       // register r of sub-block kb holds key kb*32 + (r/8)*16 + lg*8 + r%8 for query lq
       float mloc = -INFINITY;
+      if (sr.key0 + KT <= sr.count) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = cur_key0 + kb * 32 + (r >> 3) * 16 + lg * 8 + (r & 7);
-          const float x = key < cur_count ? s[kb][r] * p.scale_log2 : -INFINITY;
-          s[kb][r] = x;
-          mloc = fmaxf(mloc, x);
-        }
+          for (int r = 0; r < 16; ++r) {
+            s[kb][r] *= p.scale_log2;
+            mloc = fmaxf(mloc, s[kb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = sr.key0 + kb * 32 + (r >> 3) * 16 + lg * 8 + (r & 7);
+            s[kb][r] = key < sr.count ? s[kb][r] * p.scale_log2 : -INFINITY;
+            mloc = fmaxf(mloc, s[kb][r]);
+          }
+      }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      float lsum = 0.f;
+      // keep the reference max unless it would let exponents exceed 2^kRescale
+      const bool grow = mloc > m_run + kRescale;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mloc : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2f(s[kb][r] - m_use);
+          const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
           s[kb][r] = e;
-          lsum += e;
+          l_run += e;
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           bf16x8_t pf;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = __builtin_bit_cast(__bf16, f2bf(s[kb][h * 8 + e]));
+          for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[kb][h * 8 + e];
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const bf16x8_t vf =
-                *(const bf16x8_t*)&Vs[cur][(dt * 32 + lq) * VLD + kb * 32 + h * 16 + lg * 8];
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[dt], 0, 0, 0);
-          }
+          for (int dt = 0; dt < D / 32; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Vb[vslot(dt * 32 + lq, kb * 4 + h * 2 + lg)], pf,
+                                                            o[dt], 0, 0, 0);
         }
     }
     if (t + 1 < t1) sstore(cur ^ 1);
@@ -247,30 +250,35 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnP p) {
   }
 }
 
-// Merges split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Merges split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, where
+// m_s is each split's reference max.  8 rows per workgroup, 4 dims per thread.
 template <class T>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ opart,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
                                                            const float* __restrict__ ml, int splits,
-                                                           int B, int nq, int L, int d, T* __restrict__ o) {
-  const int row = blockIdx.x;  // (b, head, l)
-  const int l = row % L, bh = row / L, head = bh % nq, b = bh / nq;
+                                                           int B, int nq, int L, T* __restrict__ o) {
   const size_t rows = (size_t)B * nq * L;
+  const size_t row = (size_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= rows) return;
+  const int d0 = (threadIdx.x & 31) * 4;
+  const int l = (int)(row % L);
+  const size_t bh = row / L;
+  const int head = (int)(bh % nq), b = (int)(bh / nq);
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(s * rows + row) * 2]);
   float den = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < splits; ++s) {
     const float ms = ml[(s * rows + row) * 2];
-    if (ms != -INFINITY) den += exp2f(ms - M) * ml[(s * rows + row) * 2 + 1];
+    if (ms == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(ms - M);
+    den += w * ml[(s * rows + row) * 2 + 1];
+    const f32x4_t v = *(const f32x4_t*)(opart + (s * rows + row) * D + d0);
+    acc += w * v;
   }
   const float inv = 1.0f / den;
-  for (int dd = threadIdx.x; dd < d; dd += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float ms = ml[(s * rows + row) * 2];
-      if (ms != -INFINITY) acc += exp2f(ms - M) * opart[(s * rows + row) * d + dd];
-    }
-    Elem<T>::st(o + ((size_t)b * L + l) * (size_t)(nq * d) + (size_t)head * d + dd, acc * inv);
-  }
+  T* dst = o + ((size_t)b * L + l) * (size_t)(nq * D) + (size_t)head * D + d0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Elem<T>::st(dst + e, acc[e] * inv);
 }
 
 // ---- f32 path: one wave per (b, head, query); keys split over lanes ------------------------
@@ -390,8 +398,9 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     ProfScope prof("attn_combine", st);
-    hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(a.B * a.nq * a.L), dim3(128), 0, st, p.opart,
-                       p.mlpart, p.splits, a.B, a.nq, a.L, D, (bf16_t*)a.o);
+    const size_t nrows = (size_t)a.B * a.nq * a.L;
+    hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3((unsigned)((nrows + 7) / 8)), dim3(256), 0, st,
+                       p.opart, p.mlpart, p.splits, a.B, a.nq, a.L, (bf16_t*)a.o);
     return hipGetLastError();
   }
   const int rows = a.B * a.nq * a.L;

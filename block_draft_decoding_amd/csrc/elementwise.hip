@@ -23,34 +23,31 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   for (int k = threadIdx.x; k < H; k += blockDim.x) dst[k] = Elem<T>::ld(src + k);
 }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-  const int nw = blockDim.x >> 6;
-  for (int i = 0; i < nw; ++i) t += red[i];
-  return t;
-}
-
-// One workgroup per output row: y = x / sqrt(mean(x^2) + eps) * g.
+// One wavefront per output row (4 rows per workgroup), float4 loads:
+// y = x / sqrt(mean(x^2) + eps) * g.  H is a multiple of 64.
 template <class T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, int per,
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, int rows, int per,
                                                       int in_stride, int in_off, const T* __restrict__ g,
                                                       float eps, T* __restrict__ y) {
-  __shared__ float red[4];
-  const int r = blockIdx.x;
-  const float* src = x + ((size_t)(r / per) * in_stride + in_off + r % per) * H;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const f32x4_t* src = (const f32x4_t*)(x + ((size_t)(r / per) * in_stride + in_off + r % per) * H);
+  const int n4 = H / 4;
   float ss = 0.f;
-  for (int k = threadIdx.x; k < H; k += blockDim.x) {
-    const float v = src[k];
-    ss += v * v;
+  for (int k = lane; k < n4; k += 64) {
+    const f32x4_t v = src[k];
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
-  const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)H + eps);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
   T* dst = y + (size_t)r * H;
-  for (int k = threadIdx.x; k < H; k += blockDim.x) Elem<T>::st(dst + k, src[k] * inv * Elem<T>::ld(g + k));
+  for (int k = lane; k < n4; k += 64) {
+    const f32x4_t v = src[k];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Elem<T>::st(dst + 4 * k + e, v[e] * inv * Elem<T>::ld(g + 4 * k + e));
+  }
 }
 
 // X[b*C + c, t*H + k] = feats[b, t, c, k], copied in 16-byte chunks.
@@ -94,11 +91,12 @@ hipError_t rmsnorm_rows(int dt, const float* x, int H, int rows, int per, int in
                         const void* g, float eps, void* y, hipStream_t st) {
   ProfScope prof("rmsnorm", st);
   if (rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((rows + 3) / 4);
   if (dt == FPD_DTYPE_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, x, H, per, in_stride, in_off,
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, x, H, rows, per, in_stride, in_off,
                        (const bf16_t*)g, eps, (bf16_t*)y);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, x, H, per, in_stride, in_off,
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(grid), dim3(256), 0, st, x, H, rows, per, in_stride, in_off,
                        (const float*)g, eps, (float*)y);
   return hipGetLastError();
 }
