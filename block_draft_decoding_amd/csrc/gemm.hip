@@ -21,7 +21,6 @@ namespace fpd {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDSW = BK + 8;  // padded LDS row (bf16 elements): conflict-free 16-byte reads
 
 // ---- B-row maps -------------------------------------------------------------
 struct MapPlain {  // logical column n -> W row n
@@ -103,22 +102,68 @@ struct EpiGlu {
 };
 
 // ---- bf16 MFMA kernel ---------------------------------------------------------
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool PAIRED, class Map, class Epi>
+// Operand tiles go global -> LDS directly (global_load_lds_dwordx4: lane i of
+// a wave instruction fills 16-byte slot base + i) through a STAGES-deep ring,
+// so several K-tiles are in flight per workgroup without register staging.
+// A tile row (BK bf16 = CH chunks of 16 bytes) keeps chunk c at position
+// c ^ ((row / (16 / CH)) % CH): the MFMA operand reads (16 rows x 16 bytes
+// per LDS cycle) then hit distinct banks.  The swizzle is applied by choosing which
+// global chunk each lane loads.  Lanes whose row lies outside the problem
+// load a clamped in-range row instead of being switched off, so every wave
+// issues the same number of loads per stage and vmcnt counts stay exact; the
+// outputs of those rows/columns are never stored.
+template <int CH>  // 16-byte chunks per row (BK / 8)
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * CH + (c ^ ((r / (16 / CH)) & (CH - 1)));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// makes the compiler wait for every outstanding load (vmcnt(0)), which would
+// drain the stages in flight.  LDS hand-over is ordered by the explicit
+// vmcnt wait before it; the clobber keeps LDS accesses from moving across.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits until at most `ahead` later stages (LPS loads each) are outstanding.
+template <int LPS, int MAXA>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) {
+      wait_vmcnt<LPS * MAXA>();
+      return;
+    }
+    wait_stages<LPS, MAXA - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool PAIRED, class Map, class Epi>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, Map map,
     int ncols, Epi epi, float* __restrict__ partial, int part_ld, int m_tiles, int n_tiles,
     int splits) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int NT = 64 * NW;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CH = BM * (BK / 8) / NT;  // 16-byte chunks per thread
-  constexpr int B_CH = BN * (BK / 8) / NT;
-  static_assert(TM >= 1 && TN >= 1 && A_CH >= 1 && B_CH >= 1, "tile shape");
+  constexpr int CH = BK / 8;        // 16-byte chunks per tile row
+  constexpr int AI = BM * CH / NT;  // load instructions per wave and stage (A)
+  constexpr int BI = BN * CH / NT;  // (B)
+  constexpr int LPS = AI + BI;
+  static_assert(BK == 32 || BK == 64, "K tile");
+  static_assert(TM >= 1 && TN >= 1 && AI >= 1 && BI >= 1 && BM * CH % NT == 0 && BN * CH % NT == 0, "tile shape");
   static_assert(!PAIRED || (TN % 2 == 0), "paired epilogues need an even number of N sub-tiles");
+  static_assert(STAGES >= 2 && STAGES <= 8 && LPS * (STAGES - 2) < 64, "pipeline depth");
   constexpr int CPT = PAIRED ? BN / 2 : BN;  // logical columns per tile
+  constexpr int STAGE = (BM + BN) * CH;      // 16-byte slots per stage
 
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDSW];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDSW];
+  __shared__ u32x4_t lds[STAGES * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -131,34 +176,39 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   const int KT = K / BK;
   const int kt0 = (int)((long)ks * KT / splits), kt1 = (int)((long)(ks + 1) * KT / splits);
 
-  // per-thread source rows of its A and B chunks (null = zero fill)
-  const bf16_t* aptr[A_CH];
-  int akc[A_CH], alds[A_CH];
+  // per lane: source address (chunk included) of each load instruction
+  const bf16_t* asrc[AI];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT, row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-    const int m = m0 + row;
-    aptr[i] = m < M ? A + (size_t)m * lda : nullptr;
-    akc[i] = kc;
-    alds[i] = row * LDSW + kc;
+  for (int i = 0; i < AI; ++i) {
+    const int sl = (wave * AI + i) * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
+    const int m = min(m0 + r, M - 1);
+    asrc[i] = A + (size_t)m * lda + c * 8;
   }
-  const bf16_t* bptr[B_CH];
-  int bkc[B_CH], blds[B_CH];
+  const bf16_t* bsrc[BI];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * NT, row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-    int wrow = -1;
+  for (int i = 0; i < BI; ++i) {
+    const int sl = (wave * BI + i) * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
+    int wrow;
     if constexpr (PAIRED) {
-      const int p = c0 + (row % (BN / 2));
-      if (p < ncols) wrow = row < BN / 2 ? map.first(p) : map.second(p);
+      const int pidx = min(c0 + (r % (BN / 2)), ncols - 1);
+      wrow = r < BN / 2 ? map.first(pidx) : map.second(pidx);
     } else {
-      const int n = c0 + row;
-      if (n < ncols) wrow = map.row(n);
+      wrow = map.row(min(c0 + r, ncols - 1));
     }
-    bptr[i] = wrow >= 0 ? W + (size_t)wrow * K : nullptr;
-    bkc[i] = kc;
-    blds[i] = row * LDSW + kc;
+    bsrc[i] = W + (size_t)wrow * K + c * 8;
   }
+  auto issue = [&](int kt, int stage) {
+    const int k0 = kt * BK;
+    typedef __attribute__((address_space(3))) void lds_t;
+    u32x4_t* base = lds + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + k0), (lds_t*)(base + (wave * AI + i) * 64), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + k0), (lds_t*)(base + BM * CH + (wave * BI + i) * 64), 16,
+                                       0, 0);
+  };
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -168,24 +218,6 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4_t ra[A_CH], rb[B_CH];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      ra[i] = aptr[i] ? *(const u32x4_t*)(aptr[i] + k0 + akc[i]) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      rb[i] = bptr[i] ? __builtin_nontemporal_load((const u32x4_t*)(bptr[i] + k0 + bkc[i]))
-                      : u32x4_t{0, 0, 0, 0};
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) *(u32x4_t*)&As[buf][alds[i]] = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) *(u32x4_t*)&Bs[buf][blds[i]] = rb[i];
-  };
-
   int bcol[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -194,33 +226,39 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     else
       bcol[j] = wn * WN + j * 32;
   }
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int lr = lane & 31, lk = lane >> 5;
 
-  if (kt0 < kt1) {
-    gload(kt0);
-    sstore(0);
-    __syncthreads();
-  }
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    if (kt + 1 < kt1) gload(kt + 1);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[TM], bfv[TN];
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (kt0 + s < kt1) issue(kt0 + s, s);
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    // loads of stage kt are done once at most (number of later stages in flight) x LPS remain
+    wait_stages<LPS, STAGES - 2>(min(STAGES - 2, kt1 - 1 - kt));
+    barrier_nofence();  // every wave's loads of stage kt landed; stage kt-1 is free again
+    if (kt + STAGES - 1 < kt1) issue(kt + STAGES - 1, (kt - kt0 + STAGES - 1) % STAGES);
+    const u32x4_t* As = lds + ((kt - kt0) % STAGES) * STAGE;
+    const u32x4_t* Bs = As + BM * CH;
+    // operand fragments double-buffered across k-steps: the reads of step
+    // kk+1 are in flight while the MFMAs of step kk run
+    bf16x8_t af[2][TM], bfv[2][TN];
+    auto fetch = [&](int kk, int buf) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *(const bf16x8_t*)&As[cur][(wm * WM + i * 32 + lr) * LDSW + kk * 16 + lk];
+        af[buf][i] = __builtin_bit_cast(bf16x8_t, As[swz<CH>(wm * WM + i * 32 + lr, kk * 2 + lk)]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfv[j] = *(const bf16x8_t*)&Bs[cur][(bcol[j] + lr) * LDSW + kk * 16 + lk];
+      for (int j = 0; j < TN; ++j) bfv[buf][j] = __builtin_bit_cast(bf16x8_t, Bs[swz<CH>(bcol[j] + lr, kk * 2 + lk)]);
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfv[kk & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < kt1) sstore(cur ^ 1);
-    __syncthreads();
   }
 
   // epilogue: lane holds column (lane % 32) and rows (r/4)*8 + (lane/32)*4 + r%4 of each sub-tile
@@ -354,39 +392,60 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 // ---- launch helpers ---------------------------------------------------------------------
+template <int BM, int BN, int BKT, int WMW, int WNW, int S, bool PAIRED, class Map, class Epi>
+void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, const bf16_t* w, Map map, int ncols,
+                int nw, Epi epi, float* part, hipStream_t st) {
+  const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, PAIRED, Map, Epi>), dim3(grid), dim3(64 * WMW * WNW), 0,
+                     st, a, lda, M, K, w, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
+}
+
 template <bool PAIRED, class Map, class Epi>
-hipError_t run_bf16(const void* A, int lda, int M, int K, const void* W, Map map, int ncols, int nw,
-                    Epi epi, float* partial, size_t partial_bytes, hipStream_t st, const char* tag) {
-  GemmPlan pl = plan_gemm_bf16(M, ncols, K, nw, PAIRED);
-  if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) pl.splits = 1;
+hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int K, const void* W, Map map,
+                         int ncols, int nw, Epi epi, float* partial, hipStream_t st, const char* tag) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   if (grid == 0) return hipSuccess;
   const bf16_t* a = (const bf16_t*)A;
   const bf16_t* w = (const bf16_t*)W;
   float* part = pl.splits > 1 ? partial : nullptr;
   {
-  ProfScope prof(tag, st);
-  if (pl.bm == 128) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, PAIRED, Map, Epi>), dim3(grid), dim3(256),
-                       0, st, a, lda, M, K, w, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles,
-                       pl.splits);
-  } else if (pl.bm == 64) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<64, 128, 2, 2, PAIRED, Map, Epi>), dim3(grid), dim3(256),
-                       0, st, a, lda, M, K, w, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles,
-                       pl.splits);
-  } else {
-    hipLaunchKernelGGL((gemm_bf16_kernel<32, 128, 1, 2, PAIRED, Map, Epi>), dim3(grid), dim3(128),
-                       0, st, a, lda, M, K, w, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles,
-                       pl.splits);
-  }
+    ProfScope prof(tag, st);
+    switch (pl.cfg) {
+#define FPD_CFG(E, BM, BN, BKT, WMW, WNW, S) \
+  case E: launch_cfg<BM, BN, BKT, WMW, WNW, S, PAIRED>(pl, a, lda, M, K, w, map, ncols, nw, epi, part, st); break;
+      FPD_CFG(GEMM_128x128_S3, 128, 128, 64, 2, 2, 3)
+      FPD_CFG(GEMM_128x128_S2, 128, 128, 64, 2, 2, 2)
+      FPD_CFG(GEMM_64x128_S3, 64, 128, 64, 2, 2, 3)
+      FPD_CFG(GEMM_64x128_S4, 64, 128, 64, 2, 2, 4)
+      FPD_CFG(GEMM_32x128_S4, 32, 128, 64, 1, 2, 4)
+      FPD_CFG(GEMM_128x256_S2, 128, 256, 64, 2, 2, 2)
+      FPD_CFG(GEMM_64x256_S3, 64, 256, 64, 1, 4, 3)
+      FPD_CFG(GEMM_128x128_K32_S3, 128, 128, 32, 2, 2, 3)
+      FPD_CFG(GEMM_128x128_K32_S4, 128, 128, 32, 2, 2, 4)
+      FPD_CFG(GEMM_64x128_K32_S4, 64, 128, 32, 2, 2, 4)
+      FPD_CFG(GEMM_32x128_K32_S6, 32, 128, 32, 1, 2, 6)
+#undef FPD_CFG
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   ProfScope prof("splitk_reduce", st);
   const size_t n = (size_t)M * ncols;
-  hipLaunchKernelGGL((splitk_reduce_kernel<PAIRED, Map, Epi>), dim3((unsigned)((n + 255) / 256)),
-                     dim3(256), 0, st, partial, pl.splits, M, nw, ncols, map, epi);
+  hipLaunchKernelGGL((splitk_reduce_kernel<PAIRED, Map, Epi>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     partial, pl.splits, M, nw, ncols, map, epi);
   return hipGetLastError();
+}
+
+template <bool PAIRED, class Map, class Epi>
+hipError_t run_bf16(const void* A, int lda, int M, int K, const void* W, Map map, int ncols, int nw, Epi epi,
+                    float* partial, size_t partial_bytes, hipStream_t st, const char* tag) {
+  GemmPlan pl = plan_gemm_bf16(M, ncols, K, nw, PAIRED);
+  if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) {
+    pl.splits = 1;
+    pl.partial_floats = 0;
+  }
+  return run_bf16_plan<PAIRED>(pl, A, lda, M, K, W, map, ncols, nw, epi, partial, st, tag);
 }
 
 template <bool PAIRED, class Map, class Epi>
@@ -403,20 +462,50 @@ hipError_t run_f32(const void* A, int lda, int M, int K, const void* W, Map map,
 
 }  // namespace
 
-GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
+int gemm_cfg_rows(int cfg) {
+  switch (cfg) {
+    case GEMM_128x128_S3: case GEMM_128x128_S2: case GEMM_128x256_S2: case GEMM_128x128_K32_S3:
+    case GEMM_128x128_K32_S4: return 128;
+    case GEMM_64x128_S3: case GEMM_64x128_S4: case GEMM_64x256_S3: case GEMM_64x128_K32_S4: return 64;
+    default: return 32;
+  }
+}
+int gemm_cfg_bk(int cfg) { return cfg >= GEMM_128x128_K32_S3 ? 32 : 64; }
+int gemm_cfg_cols(int cfg) {
+  return (cfg == GEMM_128x256_S2 || cfg == GEMM_64x256_S3) ? 256 : 128;
+}
+
+GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int splits) {
   GemmPlan p;
-  p.bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
-  // prefer 64-row tiles when 128-row tiles leave the GPU under-filled
-  const int cpt = paired ? 64 : 128;
+  p.cfg = cfg;
+  const int bm = gemm_cfg_rows(cfg), cpt = gemm_cfg_cols(cfg) / (paired ? 2 : 1);
+  p.m_tiles = (M + bm - 1) / bm;
   p.n_tiles = (ncols + cpt - 1) / cpt;
-  if (p.bm == 128 && ((M + 127) / 128) * p.n_tiles < 256) p.bm = 64;
-  p.m_tiles = (M + p.bm - 1) / p.bm;
-  const int kt = K / BK;
-  int tiles = p.m_tiles * p.n_tiles;
-  p.splits = 1;
-  while (tiles * p.splits < 320 && kt / (p.splits * 2) >= 4) p.splits *= 2;
+  p.splits = std::max(1, std::min(splits, K / gemm_cfg_bk(cfg)));
   p.partial_floats = p.splits > 1 ? (size_t)p.splits * M * nw : 0;
   return p;
+}
+
+// Tile and split choice, from measured sweeps on MI355X (block rows M = 16,
+// 25 and 385 of the 2560-wide drafter): small M streams the weights with
+// many split-K workgroups; large M takes 128x128 tiles when they fill the
+// GPU, otherwise 64-row tiles (paired outputs) or 128x128 tiles split along K
+// (narrow plain outputs).
+GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
+  const int kt = K / 64;
+  auto with_splits = [&](int cfg, int lo, int hi) {
+    GemmPlan p = make_plan(cfg, M, ncols, K, nw, paired, 1);
+    const int tiles = p.m_tiles * p.n_tiles;
+    int s2 = 1;
+    while (tiles * s2 < lo && s2 * 2 <= 32 && kt / (s2 * 2) >= 2 && tiles * s2 * 2 <= hi) s2 *= 2;
+    return make_plan(cfg, M, ncols, K, nw, paired, s2);
+  };
+  if (M <= 32) return with_splits(GEMM_32x128_S4, 1024, 2048);
+  if (M <= 64) return with_splits(GEMM_64x128_S3, 1024, 2048);
+  const GemmPlan big = make_plan(GEMM_128x128_S2, M, ncols, K, nw, paired, 1);
+  if (big.m_tiles * big.n_tiles >= 448) return big;
+  if (paired) return with_splits(GEMM_64x128_S3, 256, 640);
+  return with_splits(GEMM_128x128_S2, 256, 640);
 }
 
 hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const void* W, int N,

@@ -22,11 +22,31 @@ class ProfScope {
 };
 
 // ---- GEMM planning (shared by workspace sizing and launches) --------------
+// Tile configurations of the bf16 GEMM: rows x columns per workgroup and
+// the depth of the global -> LDS ring.
+enum GemmCfg {
+  GEMM_128x128_S3 = 0,
+  GEMM_128x128_S2,
+  GEMM_64x128_S3,
+  GEMM_64x128_S4,
+  GEMM_32x128_S4,
+  GEMM_128x256_S2,
+  GEMM_64x256_S3,
+  GEMM_128x128_K32_S3,
+  GEMM_128x128_K32_S4,
+  GEMM_64x128_K32_S4,
+  GEMM_32x128_K32_S6,
+  GEMM_NUM_CFGS
+};
 struct GemmPlan {
-  int bm = 128;       // rows per workgroup tile
+  int cfg = GEMM_128x128_S2;
   int m_tiles = 1, n_tiles = 1, splits = 1;
   size_t partial_floats = 0;  // split-K scratch (splits * M * N_w floats) when splits > 1
 };
+GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int splits);
+int gemm_cfg_rows(int cfg);
+int gemm_cfg_cols(int cfg);
+int gemm_cfg_bk(int cfg);
 // M rows, ncols logical output columns (pairs for paired epilogues), K depth,
 // nw = W rows covered (partial row length), paired = two W rows per column.
 GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired);
