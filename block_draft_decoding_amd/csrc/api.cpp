@@ -188,6 +188,7 @@ int32_t fpd_drafter_create(const fpd_config* cfg, const fpd_weights* w, fpd_draf
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return fail(FPD_E_ARG, "rms_eps >= 0 and rope_theta > 0 required");
   if (c.hidden % 64 || c.inter % 64 || (c.n_q * c.head_dim) % 64)
     return fail(FPD_E_UNSUPPORTED, "hidden, inter and n_q*head_dim must be multiples of 64");
+  if (c.hidden > 4096) return fail(FPD_E_UNSUPPORTED, "hidden above 4096 is not supported");
   if (c.dtype == FPD_DTYPE_BF16 && c.head_dim != 128)
     return fail(FPD_E_UNSUPPORTED, "bf16 drafters need head_dim 128");
   if (c.dtype == FPD_DTYPE_F32 && c.head_dim != 64 && c.head_dim != 128)
@@ -398,11 +399,11 @@ int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, 
   float* h = (float*)wsp(ws, w.h);
   void* a = wsp(ws, w.a);
   float* part = (float*)wsp(ws, w.partial);
-  FPD_TRY_HIP(embed_gather(dt, tokens, M, d->w.embed, H, c.vocab, h, s));
+  // h = E[tokens], a = RMSNorm(h) (the first layer's attention norm)
+  FPD_TRY_HIP(embed_norm(dt, tokens, M, d->w.embed, H, c.vocab, h, d->layers[0].g_attn, c.rms_eps, a, s));
   const size_t ctx_layer = (size_t)B * c.n_kv * (size_t)ctx_cap * dh * d->esz;
   for (int li = 0; li < c.n_layers; ++li) {
     const fpd_layer_weights& lw = d->layers[li];
-    FPD_TRY_HIP(rmsnorm_rows(dt, h, H, M, M, 0, 0, lw.g_attn, c.rms_eps, a, s));
     QkvOut qo{};
     qo.q = wsp(ws, w.q), qo.k = wsp(ws, w.kb), qo.vt = wsp(ws, w.vbt);
     qo.L = L, qo.Lp = round8(L), qo.nq = c.n_q, qo.nkv = c.n_kv, qo.d = dh, qo.pos0 = block_pos;
@@ -416,14 +417,17 @@ int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, 
     at.B = B, at.L = L, at.Lp = qo.Lp, at.C = C, at.cap = ctx_cap, at.nq = c.n_q, at.nkv = c.n_kv, at.d = dh;
     at.scale = (float)(1.0 / std::sqrt((double)dh));
     FPD_TRY_HIP(attention(dt, at, wsp(ws, w.attn), w.attn_bytes, s));
-    FPD_TRY_HIP(gemm_residual(dt, at.o, qd, M, qd, lw.w_o, H, h, H, part, w.partial_bytes, s, "gemm_o"));
-    FPD_TRY_HIP(rmsnorm_rows(dt, h, H, M, M, 0, 0, lw.g_mlp, c.rms_eps, a, s));
+    // h += O W_o^T, a = RMSNorm(h) for the MLP
+    FPD_TRY_HIP(gemm_residual_norm(dt, at.o, M, qd, lw.w_o, H, h, lw.g_mlp, c.rms_eps, a, 0, part, w.partial_bytes, s,
+                                   "gemm_o"));
     void* u = wsp(ws, w.u);
     FPD_TRY_HIP(gemm_swiglu(dt, a, M, H, lw.w_gu, c.inter, u, part, w.partial_bytes, s));
-    FPD_TRY_HIP(gemm_residual(dt, u, c.inter, M, c.inter, lw.w_d, H, h, H, part, w.partial_bytes, s,
-                              "gemm_down"));
+    // h += u W_d^T, then the next layer's attention norm, or the final norm over positions 1..L-1
+    const bool last = li + 1 == c.n_layers;
+    FPD_TRY_HIP(gemm_residual_norm(dt, u, M, c.inter, lw.w_d, H, h, last ? d->w.g_final : d->layers[li + 1].g_attn,
+                                   c.rms_eps, last ? hidden_out : a, last ? L : 0, part, w.partial_bytes, s,
+                                   "gemm_down"));
   }
-  FPD_TRY_HIP(rmsnorm_rows(dt, h, H, B * (L - 1), L - 1, L, 1, d->w.g_final, c.rms_eps, hidden_out, s));
   return FPD_OK;
 }
 

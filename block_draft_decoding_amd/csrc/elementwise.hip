@@ -50,6 +50,116 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// stores 4 normalised values x * inv * g at dst[0..3] (bf16: one 8-byte store)
+template <class T>
+__device__ __forceinline__ void store_norm4(T* dst, f32x4_t v, float inv, const T* g);
+template <>
+__device__ __forceinline__ void store_norm4<bf16_t>(bf16_t* dst, f32x4_t v, float inv, const bf16_t* g) {
+  const u32x2_t gw = *(const u32x2_t*)g;
+  u32x2_t w;
+  w[0] = pack_bf16x2(v[0] * inv * __uint_as_float(gw[0] << 16), v[1] * inv * __uint_as_float(gw[0] & 0xffff0000u));
+  w[1] = pack_bf16x2(v[2] * inv * __uint_as_float(gw[1] << 16), v[3] * inv * __uint_as_float(gw[1] & 0xffff0000u));
+  *(u32x2_t*)dst = w;
+}
+template <>
+__device__ __forceinline__ void store_norm4<float>(float* dst, f32x4_t v, float inv, const float* g) {
+  const f32x4_t gg = *(const f32x4_t*)g;
+  *(f32x4_t*)dst = v * inv * gg;
+}
+
+// Fused residual update and RMSNorm, one workgroup per row: h[r] +=
+// sum_s partial[s][r] (split-K partial products, fixed split order; none when
+// partial is null), then out[row'] = RMSNorm(h[r]) * g.  With final_L > 0 only
+// rows r = b*L + l with l >= 1 produce output, at row b*(L-1) + l - 1 (the
+// drafter's final norm over the masked positions).  H is a multiple of 64
+// and at most 4096 (the row stays in registers: 4 float4 per thread).
+template <class T>
+__global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict__ partial, int splits, int M, int H,
+                                                         float* __restrict__ h, const T* __restrict__ g, float eps,
+                                                         T* __restrict__ out, int final_L) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  int orow = r;
+  if (final_L > 0) {
+    const int l = r % final_L;
+    if (l == 0) return;
+    orow = (r / final_L) * (final_L - 1) + l - 1;
+  }
+  f32x4_t* hr = (f32x4_t*)(h + (size_t)r * H);
+  const int n4 = H / 4;
+  const size_t pstride = (size_t)M * H / 4;
+  const f32x4_t* pr = partial ? (const f32x4_t*)partial + (size_t)r * n4 : nullptr;
+  f32x4_t v[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * 256;
+    if (k < n4) {
+      f32x4_t x = hr[k];
+      if (pr) {
+        f32x4_t acc = pr[k];
+        for (int s = 1; s < splits; ++s) acc += pr[s * pstride + k];
+        x += acc;
+        hr[k] = x;
+      }
+      v[i] = x;
+      ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
+  }
+  const float inv = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
+  T* dst = out + (size_t)orow * H;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * 256;
+    if (k < n4) store_norm4<T>(dst + 4 * k, v[i], inv, g + 4 * k);
+  }
+}
+
+// h[m] = E[tok[m]] (ids outside [0, V) embed as zero rows), a[m] = RMSNorm(h[m]) * g;
+// one workgroup per row, 4 elements per thread and step.
+template <class T>
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* __restrict__ tok, const T* __restrict__ E, int H,
+                                                         int V, float* __restrict__ h, const T* __restrict__ g,
+                                                         float eps, T* __restrict__ a) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int t = tok[r];
+  const bool ok = t >= 0 && t < V;
+  f32x4_t* hr = (f32x4_t*)(h + (size_t)r * H);
+  const int n4 = H / 4;
+  f32x4_t v[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * 256;
+    if (k < n4) {
+      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+      if (ok) {
+        const T* src = E + (size_t)t * H + 4 * k;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = Elem<T>::ld(src + e);
+      }
+      hr[k] = x;
+      v[i] = x;
+      ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
+  }
+  const float inv = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * 256;
+    if (k < n4) store_norm4<T>(a + (size_t)r * H + 4 * k, v[i], inv, g + 4 * k);
+  }
+}
+
 // X[b*C + c, t*H + k] = feats[b, t, c, k], copied in 16-byte chunks.
 __global__ __launch_bounds__(256) void concat_kernel(const u32x4_t* __restrict__ f, int B, int nt, int C,
                                                      int Hc, u32x4_t* __restrict__ X) {
@@ -98,6 +208,33 @@ hipError_t rmsnorm_rows(int dt, const float* x, int H, int rows, int per, int in
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(grid), dim3(256), 0, st, x, H, rows, per, in_stride, in_off,
                        (const float*)g, eps, (float*)y);
+  return hipGetLastError();
+}
+
+hipError_t residual_norm(int dt, const float* partial, int splits, int M, int H, float* h, const void* g, float eps,
+                         void* out, int final_L, hipStream_t st) {
+  ProfScope prof("resid_norm", st);
+  if (M == 0) return hipSuccess;
+  const unsigned grid = (unsigned)M;
+  if (dt == FPD_DTYPE_BF16)
+    hipLaunchKernelGGL(resid_norm_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, partial, splits, M, H, h,
+                       (const bf16_t*)g, eps, (bf16_t*)out, final_L);
+  else
+    hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(grid), dim3(256), 0, st, partial, splits, M, H, h,
+                       (const float*)g, eps, (float*)out, final_L);
+  return hipGetLastError();
+}
+
+hipError_t embed_norm(int dt, const int32_t* tokens, int M, const void* E, int H, int V, float* h, const void* g,
+                      float eps, void* a, hipStream_t st) {
+  ProfScope prof("embed_norm", st);
+  if (M == 0) return hipSuccess;
+  if (dt == FPD_DTYPE_BF16)
+    hipLaunchKernelGGL(embed_norm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, tokens, (const bf16_t*)E, H, V, h,
+                       (const bf16_t*)g, eps, (bf16_t*)a);
+  else
+    hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(M), dim3(256), 0, st, tokens, (const float*)E, H, V, h,
+                       (const float*)g, eps, (float*)a);
   return hipGetLastError();
 }
 

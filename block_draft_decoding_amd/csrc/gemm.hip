@@ -402,7 +402,8 @@ void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, cons
 
 template <bool PAIRED, class Map, class Epi>
 hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int K, const void* W, Map map,
-                         int ncols, int nw, Epi epi, float* partial, hipStream_t st, const char* tag) {
+                         int ncols, int nw, Epi epi, float* partial, hipStream_t st, const char* tag,
+                         bool reduce = true) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   if (grid == 0) return hipSuccess;
   const bf16_t* a = (const bf16_t*)A;
@@ -429,7 +430,7 @@ hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int 
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.splits == 1) return e;
+  if (e != hipSuccess || pl.splits == 1 || !reduce) return e;
   ProfScope prof("splitk_reduce", st);
   const size_t n = (size_t)M * ncols;
   hipLaunchKernelGGL((splitk_reduce_kernel<PAIRED, Map, Epi>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
@@ -524,6 +525,24 @@ hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const voi
   if (dt == FPD_DTYPE_BF16)
     return run_bf16<false>(A, lda, M, K, W, MapPlain{}, N, N, e, partial, partial_bytes, st, tag);
   return run_f32<false>(A, lda, M, K, W, MapPlain{}, N, e, st, tag);
+}
+
+hipError_t gemm_residual_norm(int dt, const void* A, int M, int K, const void* W, int H, float* h, const void* g,
+                              float eps, void* out, int final_L, float* partial, size_t partial_bytes,
+                              hipStream_t st, const char* tag) {
+  if (dt == FPD_DTYPE_BF16) {
+    GemmPlan pl = plan_gemm_bf16(M, H, K, H, false);
+    if (pl.splits > 1 && pl.partial_floats * sizeof(float) <= partial_bytes) {
+      // split-K partials; the residual sum and the RMSNorm run fused, row-wise
+      hipError_t e = run_bf16_plan<false>(pl, A, K, M, K, W, MapPlain{}, H, H, EpiResid{h, H}, partial, st, tag,
+                                          /*reduce=*/false);
+      if (e != hipSuccess) return e;
+      return residual_norm(dt, partial, pl.splits, M, H, h, g, eps, out, final_L, st);
+    }
+  }
+  hipError_t e = gemm_residual(dt, A, K, M, K, W, H, h, H, partial, partial_bytes, st, tag);
+  if (e != hipSuccess) return e;
+  return residual_norm(dt, nullptr, 1, M, H, h, g, eps, out, final_L, st);
 }
 
 hipError_t gemm_qkv(int dt, const void* A, int M, int K, const void* Wqkv, const QkvOut& o,

@@ -65,6 +65,13 @@ hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const voi
                          float* h, int ldh, float* partial, size_t partial_bytes, hipStream_t st,
                          const char* tag);
 
+// h += A W^T, then out = RMSNorm(h) * g (bf16 split-K partials are summed in
+// the fused row-wise norm kernel).  final_L > 0: output only rows with
+// l = r % final_L >= 1, at b*(L-1) + l - 1.
+hipError_t gemm_residual_norm(int dt, const void* A, int M, int K, const void* W, int H, float* h, const void* g,
+                              float eps, void* out, int final_L, float* partial, size_t partial_bytes,
+                              hipStream_t st, const char* tag);
+
 // Fused QKV projection of block rows m = b * L + l: Q [B, nq, L, d],
 // K [B, nkv, L, d] (RoPE at pos0 + l), Vt [B, nkv, d, Lp] (transposed).
 struct QkvOut {
@@ -95,6 +102,12 @@ hipError_t embed_gather(int dt, const int32_t* tokens, int M, const void* E, int
 // y[r] = RMSNorm(x[row(r)]) * g stored in dt, with row(r) = (r / per) * in_stride + in_off + r % per.
 hipError_t rmsnorm_rows(int dt, const float* x, int H, int rows, int per, int in_stride, int in_off,
                         const void* g, float eps, void* y, hipStream_t st);
+// h[r] += sum_s partial[s][r] (partial may be null), out = RMSNorm(h) * g; see gemm_residual_norm.
+hipError_t residual_norm(int dt, const float* partial, int splits, int M, int H, float* h, const void* g, float eps,
+                         void* out, int final_L, hipStream_t st);
+// h = E[tokens] (ids outside [0, V) embed as zero rows), a = RMSNorm(h) * g.
+hipError_t embed_norm(int dt, const int32_t* tokens, int M, const void* E, int H, int V, float* h, const void* g,
+                      float eps, void* a, hipStream_t st);
 // X[b * C + c, t * H + k] = feats[b, t, c, k]
 hipError_t concat_features(int dt, const void* feats, int B, int nt, int C, int H, void* X,
                            hipStream_t st);

@@ -94,7 +94,7 @@ enum {
  * (i, i + d/2), inverse frequency theta^(-2i/d)) is applied to queries and
  * keys when use_rope != 0.  RMSNorm: x / sqrt(mean(x^2) + rms_eps) * g.
  * Supported: F32 with head_dim in {64, 128}; BF16 with head_dim 128.
- * hidden, inter and n_q*head_dim must be multiples of 64.                 */
+ * hidden, inter and n_q*head_dim must be multiples of 64; hidden <= 4096. */
 typedef struct fpd_config {
   int32_t hidden, n_q, n_kv, head_dim, n_layers, inter, vocab, n_fused;
   int32_t dtype;      /* FPD_DTYPE_*                                          */

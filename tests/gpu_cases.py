@@ -16,9 +16,9 @@ from block_draft_decoding_amd import synth
 from oracle import fpd_oracle as O
 
 # Parity rules (derivation in the repository's design notes):
-#  * TOL: per-position relative L2 error ||g - o|| / ||o|| of every vector
-#    (a position's hidden state, logits, context row), the stated 2e-2
-#    (bf16) / 1e-4 (fp32) relative tolerance;
+#  * TOL: relative L2 error ||g - o|| / ||o|| of every position's vector
+#    (hidden state, legal logits, context row; positions with >= 16 entries)
+#    and of the whole tensor: the stated 2e-2 (bf16) / 1e-4 (fp32);
 #  * ELEM: elementwise outlier guard |g - o| <= ELEM * max(|o|, rms(o));
 #  * GAP: argmax must agree wherever the oracle's top-2 legal-logit gap
 #    exceeds GAP * rms of that position's legal logits.  In bf16 two faithful
@@ -61,13 +61,15 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def rel_close(got, want, dtype, what=""):
-    """Per-position relative L2 error ||g - o|| / max(||o||, sqrt(n) rms(o))
-    <= TOL[dtype] (n = finite entries of the position; the floor keeps a
-    position with a single near-zero legal logit from reading as a large
-    relative error) and elementwise |g - o| <= ELEM[dtype] * max(|o|, rms(o))
-    over the finite entries; the non-finite pattern (the -inf padding of
-    logits) must match exactly.  Returns (max per-position relative error,
-    max elementwise error relative to max(|o|, rms))."""
+    """Relative-error checks over the finite entries (the non-finite pattern,
+    i.e. the -inf padding of logits, must match exactly):
+      * per position with >= 16 entries: ||g - o|| / ||o|| <= TOL[dtype];
+      * the whole tensor: ||g - o|| / ||o|| <= TOL[dtype];
+      * every entry: |g - o| <= ELEM[dtype] * max(|o|, rms(o)).
+    Positions with fewer entries (a delimiter's single legal logit) are a
+    handful of scalars whose relative error is a single noise sample; the
+    whole-tensor and elementwise checks cover them.  Returns (max per-position
+    relative error, max elementwise error relative to max(|o|, rms))."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
@@ -78,15 +80,18 @@ def rel_close(got, want, dtype, what=""):
     g, w = got[fin], want[fin]
     rms = np.sqrt(np.mean(w * w)) if w.size else 0.0
     nfin = fin.reshape(-1, want.shape[-1]).sum(axis=1)
-    num = np.linalg.norm(g2 - w2, axis=1)
-    den = np.maximum(np.linalg.norm(w2, axis=1), np.sqrt(nfin) * rms)
-    row = np.where(den > 0, num / np.maximum(den, 1e-300), num)
-    elem = np.abs(g - w) / np.maximum(np.abs(w), rms) if w.size else np.zeros(0)
+    big = nfin >= 16
+    num = np.linalg.norm(g2 - w2, axis=1)[big]
+    den = np.linalg.norm(w2, axis=1)[big]
+    row = num / np.maximum(den, 1e-300)
     rmax = float(row.max()) if row.size else 0.0
+    whole = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-300)) if w.size else 0.0
+    elem = np.abs(g - w) / np.maximum(np.abs(w), rms) if w.size else np.zeros(0)
     emax = float(elem.max()) if elem.size else 0.0
     assert rmax <= TOL[dtype], f"{what}: per-position relative error {rmax:.3e} > {TOL[dtype]}"
+    assert whole <= TOL[dtype], f"{what}: whole-tensor relative error {whole:.3e} > {TOL[dtype]}"
     assert emax <= ELEM[dtype], f"{what}: elementwise error {emax:.3e} > {ELEM[dtype]} (rms {rms:.3g})"
-    return rmax, emax
+    return max(rmax, whole), emax
 
 
 def top2_gap(z: np.ndarray, lay: O.Layout) -> np.ndarray:
