@@ -12,6 +12,7 @@
 // members in its second half, and each wave takes matching sub-tiles from
 // both halves, so a lane holds both members of every pair in registers.
 #include <algorithm>
+#include <type_traits>
 
 #include "../../include/fpd.h"
 #include "kernels.h"
@@ -112,6 +113,37 @@ struct EpiGlu {
 // load a clamped in-range row instead of being switched off, so every wave
 // issues the same number of loads per stage and vmcnt counts stay exact; the
 // outputs of those rows/columns are never stored.
+// Maps the launch index to a tile (row tile fastest, then column tile, then
+// K split).  Each XCD runs one contiguous range of tiles (workgroups are
+// dispatched to XCDs round-robin), so the row tiles that share a weight tile
+// meet in that XCD's L2.  Within the range, tiles whose rows all lie below M
+// go first and the last, partly filled row tile of each column (cheap: its
+// empty row blocks are skipped) goes last, where it fills the gaps the full
+// tiles leave.  m_full = number of full row tiles (m_tiles or m_tiles - 1).
+__device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, int m_full) {
+  const int x = bid % kXcds, local = bid / kXcds;
+  const int per = grid / kXcds, rem = grid % kXcds;
+  const int s = x * per + (x < rem ? x : rem);
+  const int cnt = per + (x < rem ? 1 : 0);
+  if (m_full == m_tiles) return s + local;
+  auto full_before = [&](int t) { return (t / m_tiles) * m_full + min(t % m_tiles, m_full); };
+  const int h0 = full_before(s), h1 = full_before(s + cnt);
+  if (local < h1 - h0) {
+    const int i = h0 + local;
+    return (i / m_full) * m_tiles + i % m_full;
+  }
+  return (s - h0 + local - (h1 - h0)) * m_tiles + m_full;
+}
+
+// One 16-byte buffer load per lane written straight into LDS: lane i fills
+// the 16 bytes at dst + 16 i (dst is wave-uniform).  Only the device pass
+// sees the builtin; the host pass would otherwise drop the kernel stubs.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, u32x4_t* dst, uint32_t voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+#endif
+}
+
 template <int CH>  // 16-byte chunks per row (BK / 8)
 __device__ __forceinline__ int swz(int r, int c) {
   return r * CH + (c ^ ((r / (16 / CH)) & (CH - 1)));
@@ -122,6 +154,12 @@ __device__ __forceinline__ int swz(int r, int c) {
 // drain the stages in flight.  LDS hand-over is ordered by the explicit
 // vmcnt wait before it; the clobber keeps LDS accesses from moving across.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt fields at their maximum), issued
+// as the builtin so that the compiler's own wait insertion sees it: scalar
+// loads still pending make it treat the LDS counter as out of order and
+// fall back to full waits before every MFMA group.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -145,7 +183,7 @@ __device__ __forceinline__ void wait_stages(int ahead) {
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool PAIRED, class Map, class Epi>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, Map map,
+    const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, int w_rows, Map map,
     int ncols, Epi epi, float* __restrict__ partial, int part_ld, int m_tiles, int n_tiles,
     int splits) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -159,15 +197,16 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   static_assert(BK == 32 || BK == 64, "K tile");
   static_assert(TM >= 1 && TN >= 1 && AI >= 1 && BI >= 1 && BM * CH % NT == 0 && BN * CH % NT == 0, "tile shape");
   static_assert(!PAIRED || (TN % 2 == 0), "paired epilogues need an even number of N sub-tiles");
-  static_assert(STAGES >= 2 && STAGES <= 8 && LPS * (STAGES - 2) < 64, "pipeline depth");
+  static_assert(STAGES >= 2 && STAGES <= 8 && LPS * (STAGES - 1) < 64, "pipeline depth");
   constexpr int CPT = PAIRED ? BN / 2 : BN;  // logical columns per tile
   constexpr int STAGE = (BM + BN) * CH;      // 16-byte slots per stage
 
   __shared__ u32x4_t lds[STAGES * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = gemm_tile_order(blockIdx.x, gridDim.x, m_tiles, M / BM);
   const int mt = tile % m_tiles;
   const int rest = tile / m_tiles;
   const int nt = rest % n_tiles;
@@ -176,15 +215,23 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   const int KT = K / BK;
   const int kt0 = (int)((long)ks * KT / splits), kt1 = (int)((long)(ks + 1) * KT / splits);
 
-  // per lane: source address (chunk included) of each load instruction
-  const bf16_t* asrc[AI];
+  // Operands are read through buffer descriptors: the per-lane byte offset
+  // (row and swizzled chunk) is fixed, the K-tile offset is a scalar.  The
+  // LDS-writing buffer load is also what lets the compiler keep its LDS read
+  // waits partial (an LDS-writing global load counts as a flat access, which
+  // forces a full LDS wait before every MFMA group).
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)((size_t)M * lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)((size_t)w_rows * K * 2), 0x00020000);
+  uint32_t aoff[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int sl = (wave * AI + i) * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
     const int m = min(m0 + r, M - 1);
-    asrc[i] = A + (size_t)m * lda + c * 8;
+    aoff[i] = (uint32_t)(((size_t)m * lda + c * 8) * 2);
   }
-  const bf16_t* bsrc[BI];
+  uint32_t boff[BI];
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
     const int sl = (wave * BI + i) * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
@@ -195,19 +242,15 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     } else {
       wrow = map.row(min(c0 + r, ncols - 1));
     }
-    bsrc[i] = W + (size_t)wrow * K + c * 8;
+    boff[i] = (uint32_t)(((size_t)wrow * K + c * 8) * 2);
   }
   auto issue = [&](int kt, int stage) {
-    const int k0 = kt * BK;
-    typedef __attribute__((address_space(3))) void lds_t;
+    const int soff = kt * BK * 2;
     u32x4_t* base = lds + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < AI; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + k0), (lds_t*)(base + (wave * AI + i) * 64), 16, 0, 0);
+    for (int i = 0; i < AI; ++i) lds_dma16(arsrc, base + (wave * AI + i) * 64, aoff[i], soff);
 #pragma unroll
-    for (int i = 0; i < BI; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + k0), (lds_t*)(base + BM * CH + (wave * BI + i) * 64), 16,
-                                       0, 0);
+    for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + BM * CH + (wave * BI + i) * 64, boff[i], soff);
   };
 
   f32x16_t acc[TM][TN];
@@ -228,36 +271,82 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   }
   const int lr = lane & 31, lk = lane >> 5;
 
+  // Row blocks of this wave that contain rows below M (wave-uniform).  The
+  // blocks past M are neither read nor multiplied (their outputs are never
+  // stored), so a tile that only covers the last rows of M costs a fraction
+  // of a full tile; its waves still take part in the loads and barriers.
+  const int rows_left = M - (m0 + wm * WM);
+  const int nr = rows_left >= WM ? TM : (rows_left <= 0 ? 0 : (rows_left + 31) / 32);
+
+  // The ring holds STAGES K-tiles.  Within a K-tile the operand fragments of
+  // step kk+1 are read from LDS while the MFMAs of step kk run (two register
+  // sets, order pinned by scheduling barriers).  At the last step each wave
+  // drains its own LDS reads and waits for its loads of the next K-tile; one
+  // barrier then hands the finished stage back to the loads (K-tile kt +
+  // STAGES goes into it) and publishes the next K-tile, whose first fragments
+  // are read before the last MFMAs of the current one.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < STAGES; ++s)
     if (kt0 + s < kt1) issue(kt0 + s, s);
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    // loads of stage kt are done once at most (number of later stages in flight) x LPS remain
-    wait_stages<LPS, STAGES - 2>(min(STAGES - 2, kt1 - 1 - kt));
-    barrier_nofence();  // every wave's loads of stage kt landed; stage kt-1 is free again
-    if (kt + STAGES - 1 < kt1) issue(kt + STAGES - 1, (kt - kt0 + STAGES - 1) % STAGES);
-    const u32x4_t* As = lds + ((kt - kt0) % STAGES) * STAGE;
-    const u32x4_t* Bs = As + BM * CH;
-    // operand fragments double-buffered across k-steps: the reads of step
-    // kk+1 are in flight while the MFMAs of step kk run
-    bf16x8_t af[2][TM], bfv[2][TN];
-    auto fetch = [&](int kk, int buf) {
+  auto mainloop = [&](auto nr_c) {
+    constexpr int NR = decltype(nr_c)::value;
+    constexpr int KS = BK / 16;
+    bf16x8_t af[2][TM > 0 ? TM : 1], bfv[2][TN];
+    auto fetch = [&](int stage, int kk, int buf) {
+      if constexpr (NR > 0) {
+        const u32x4_t* As = lds + stage * STAGE;
+        const u32x4_t* Bs = As + BM * CH;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[buf][i] = __builtin_bit_cast(bf16x8_t, As[swz<CH>(wm * WM + i * 32 + lr, kk * 2 + lk)]);
+        for (int i = 0; i < NR; ++i)
+          af[buf][i] = __builtin_bit_cast(bf16x8_t, As[swz<CH>(wm * WM + i * 32 + lr, kk * 2 + lk)]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfv[buf][j] = __builtin_bit_cast(bf16x8_t, Bs[swz<CH>(bcol[j] + lr, kk * 2 + lk)]);
+        for (int j = 0; j < TN; ++j) bfv[buf][j] = __builtin_bit_cast(bf16x8_t, Bs[swz<CH>(bcol[j] + lr, kk * 2 + lk)]);
+      }
     };
-    fetch(0, 0);
+    auto mma = [&](int buf) {
+      if constexpr (NR > 0) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
+        for (int i = 0; i < NR; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfv[buf][j], acc[i][j], 0, 0, 0);
+      }
+    };
+    if (kt0 >= kt1) return;
+    wait_lgkm0();
+    wait_stages<LPS, STAGES - 1>(min(STAGES - 1, kt1 - 1 - kt0));
+    barrier_nofence();
+    fetch(0, 0, 0);
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int stage = (kt - kt0) % STAGES;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfv[kk & 1][j], acc[i][j], 0, 0, 0);
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) {
+          fetch(stage, kk + 1, (kk + 1) & 1);
+        } else {
+          wait_lgkm0();
+          if (kt + 1 < kt1) wait_stages<LPS, STAGES - 2>(min(STAGES - 2, kt1 - 2 - kt));
+          barrier_nofence();
+          if (kt + STAGES < kt1) issue(kt + STAGES, stage);
+          if (kt + 1 < kt1) fetch(stage + 1 == STAGES ? 0 : stage + 1, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(kk & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if (nr == TM) {
+    mainloop(std::integral_constant<int, TM>{});
+  } else if (nr == 0) {
+    mainloop(std::integral_constant<int, 0>{});
+  } else {
+    if constexpr (TM > 1) {
+      if (nr == 1)
+        mainloop(std::integral_constant<int, 1>{});
+      else
+        mainloop(std::integral_constant<int, TM>{});
     }
   }
 
@@ -397,7 +486,7 @@ void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, cons
                 int nw, Epi epi, float* part, hipStream_t st) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, PAIRED, Map, Epi>), dim3(grid), dim3(64 * WMW * WNW), 0,
-                     st, a, lda, M, K, w, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
+                     st, a, lda, M, K, w, nw, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
 }
 
 template <bool PAIRED, class Map, class Epi>
@@ -414,17 +503,7 @@ hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int 
     switch (pl.cfg) {
 #define FPD_CFG(E, BM, BN, BKT, WMW, WNW, S) \
   case E: launch_cfg<BM, BN, BKT, WMW, WNW, S, PAIRED>(pl, a, lda, M, K, w, map, ncols, nw, epi, part, st); break;
-      FPD_CFG(GEMM_128x128_S3, 128, 128, 64, 2, 2, 3)
-      FPD_CFG(GEMM_128x128_S2, 128, 128, 64, 2, 2, 2)
-      FPD_CFG(GEMM_64x128_S3, 64, 128, 64, 2, 2, 3)
-      FPD_CFG(GEMM_64x128_S4, 64, 128, 64, 2, 2, 4)
-      FPD_CFG(GEMM_32x128_S4, 32, 128, 64, 1, 2, 4)
-      FPD_CFG(GEMM_128x256_S2, 128, 256, 64, 2, 2, 2)
-      FPD_CFG(GEMM_64x256_S3, 64, 256, 64, 1, 4, 3)
-      FPD_CFG(GEMM_128x128_K32_S3, 128, 128, 32, 2, 2, 3)
-      FPD_CFG(GEMM_128x128_K32_S4, 128, 128, 32, 2, 2, 4)
-      FPD_CFG(GEMM_64x128_K32_S4, 64, 128, 32, 2, 2, 4)
-      FPD_CFG(GEMM_32x128_K32_S6, 32, 128, 32, 1, 2, 6)
+      FPD_GEMM_CFGS(FPD_CFG)
 #undef FPD_CFG
       default: return hipErrorInvalidValue;
     }
@@ -463,18 +542,20 @@ hipError_t run_f32(const void* A, int lda, int M, int K, const void* W, Map map,
 
 }  // namespace
 
-int gemm_cfg_rows(int cfg) {
-  switch (cfg) {
-    case GEMM_128x128_S3: case GEMM_128x128_S2: case GEMM_128x256_S2: case GEMM_128x128_K32_S3:
-    case GEMM_128x128_K32_S4: return 128;
-    case GEMM_64x128_S3: case GEMM_64x128_S4: case GEMM_64x256_S3: case GEMM_64x128_K32_S4: return 64;
-    default: return 32;
-  }
-}
-int gemm_cfg_bk(int cfg) { return cfg >= GEMM_128x128_K32_S3 ? 32 : 64; }
-int gemm_cfg_cols(int cfg) {
-  return (cfg == GEMM_128x256_S2 || cfg == GEMM_64x256_S3) ? 256 : 128;
-}
+namespace {
+struct CfgShape {
+  int rows, cols, bk;
+};
+constexpr CfgShape kCfgShape[GEMM_NUM_CFGS] = {
+#define FPD_SHAPE(E, BM, BN, BKT, WMW, WNW, S) {BM, BN, BKT},
+    FPD_GEMM_CFGS(FPD_SHAPE)
+#undef FPD_SHAPE
+};
+}  // namespace
+
+int gemm_cfg_rows(int cfg) { return kCfgShape[cfg].rows; }
+int gemm_cfg_cols(int cfg) { return kCfgShape[cfg].cols; }
+int gemm_cfg_bk(int cfg) { return kCfgShape[cfg].bk; }
 
 GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int splits) {
   GemmPlan p;
@@ -488,10 +569,10 @@ GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int sp
 }
 
 // Tile and split choice, from measured sweeps on MI355X (block rows M = 16,
-// 25 and 385 of the 2560-wide drafter): small M streams the weights with
-// many split-K workgroups; large M takes 128x128 tiles when they fill the
-// GPU, otherwise 64-row tiles (paired outputs) or 128x128 tiles split along K
-// (narrow plain outputs).
+// 25 and 385 of the 2560-wide drafter, weights streamed from HBM): small M
+// streams the weights with many split-K workgroups; larger M takes the
+// 128x256 eight-wave tile when it alone nearly fills 256 CUs, else the same
+// tile split along K (deep K or paired outputs) or 64x128 tiles split along K.
 GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   const int kt = K / 64;
   auto with_splits = [&](int cfg, int lo, int hi) {
@@ -503,10 +584,10 @@ GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   };
   if (M <= 32) return with_splits(GEMM_32x128_S4, 1024, 2048);
   if (M <= 64) return with_splits(GEMM_64x128_S3, 1024, 2048);
-  const GemmPlan big = make_plan(GEMM_128x128_S2, M, ncols, K, nw, paired, 1);
-  if (big.m_tiles * big.n_tiles >= 448) return big;
-  if (paired) return with_splits(GEMM_64x128_S3, 256, 640);
-  return with_splits(GEMM_128x128_S2, 256, 640);
+  const GemmPlan big = make_plan(GEMM_128x256_W8_S3, M, ncols, K, nw, paired, 1);
+  if (big.m_tiles * big.n_tiles >= 224) return big;
+  if (paired || K >= 8192) return with_splits(GEMM_128x256_W8_S3, 160, 400);
+  return with_splits(GEMM_64x128_S3, 256, 640);
 }
 
 hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const void* W, int N,

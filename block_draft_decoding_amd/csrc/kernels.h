@@ -22,20 +22,22 @@ class ProfScope {
 };
 
 // ---- GEMM planning (shared by workspace sizing and launches) --------------
-// Tile configurations of the bf16 GEMM: rows x columns per workgroup and
-// the depth of the global -> LDS ring.
+// Tile configurations of the bf16 GEMM: workgroup tile rows x columns, K
+// tile, wave grid (rows x columns of waves) and the depth of the
+// global -> LDS ring.  X(name, rows, cols, k_tile, waves_m, waves_n, stages).
+#define FPD_GEMM_CFGS(X)                      \
+  X(GEMM_128x128_S2, 128, 128, 64, 2, 2, 2)   \
+  X(GEMM_64x128_S3, 64, 128, 64, 2, 2, 3)     \
+  X(GEMM_32x128_S4, 32, 128, 64, 1, 2, 4)     \
+  X(GEMM_64x256_S3, 64, 256, 64, 1, 4, 3)     \
+  X(GEMM_128x256_W8_S2, 128, 256, 64, 2, 4, 2) \
+  X(GEMM_128x256_W8_S3, 128, 256, 64, 2, 4, 3) \
+  X(GEMM_256x128_W8_S3, 256, 128, 64, 4, 2, 3) \
+  X(GEMM_128x256_W8_K32_S5, 128, 256, 32, 2, 4, 5)
 enum GemmCfg {
-  GEMM_128x128_S3 = 0,
-  GEMM_128x128_S2,
-  GEMM_64x128_S3,
-  GEMM_64x128_S4,
-  GEMM_32x128_S4,
-  GEMM_128x256_S2,
-  GEMM_64x256_S3,
-  GEMM_128x128_K32_S3,
-  GEMM_128x128_K32_S4,
-  GEMM_64x128_K32_S4,
-  GEMM_32x128_K32_S6,
+#define FPD_ENUM(name, ...) name,
+  FPD_GEMM_CFGS(FPD_ENUM)
+#undef FPD_ENUM
   GEMM_NUM_CFGS
 };
 struct GemmPlan {

@@ -24,6 +24,15 @@ def test_exports_every_declared_symbol():
     assert not missing, missing
 
 
+def test_every_kernel_has_a_host_launch_stub():
+    """A kernel whose host-side stub was not emitted leaves an undefined symbol
+    behind that only fails when that kernel is first launched."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", fpd.LIB_PATH], capture_output=True, text=True, check=True)
+    stubs = [l for l in out.stdout.splitlines() if "device_stub" in l]
+    assert not stubs, stubs[:3]
+
+
 def _small_schemas():
     V = 4099
     ids = dict(start_id=4095, mask_id=4098, delim_id=4080, off_id=-1, plus_id=4082, minus_id=4083,
