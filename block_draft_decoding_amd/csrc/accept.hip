@@ -27,21 +27,40 @@ __device__ __forceinline__ int wave_min(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(64) void validate_kernel(ValidateArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+// One workgroup per batch row, one thread per position.  The row's tokens
+// and (when they fit) the legal-id sets are staged in LDS first, so every
+// position's checks (set membership by binary search, the paired-position
+// rule, the digit-field automaton) run in parallel on LDS data and the row's
+// answer is a workgroup minimum over the first failing positions.
+constexpr int kValThreads = 512;
+
+__global__ __launch_bounds__(kValThreads) void validate_kernel(ValidateArgs a, int stage_tok, int stage_ids) {
+  extern __shared__ int32_t sm[];
+  __shared__ int red[kValThreads / 64];
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int P = a.L - 1;
-  const int32_t* tok = a.tokens + (size_t)b * P;
+  const int32_t* gtok = a.tokens + (size_t)b * P;
+  const int32_t* tok = gtok;
+  const int32_t* ids = a.set_ids;
+  if (stage_tok) {
+    for (int i = tid; i < P; i += kValThreads) sm[i] = gtok[i];
+    tok = sm;
+  }
+  if (stage_ids) {
+    int32_t* sid = sm + (stage_tok ? P : 0);
+    for (int i = tid; i < a.n_set_ids; i += kValThreads) sid[i] = a.set_ids[i];
+    ids = sid;
+  }
+  __syncthreads();
   int first = INT_MAX;
-  for (int p0 = 1; p0 < a.L; p0 += 64) {
-    const int p = p0 + lane;
-    if (p >= a.L) break;
+  for (int p = tid + 1; p < a.L; p += kValThreads) {
     const int t = tok[p - 1];
     const int s = a.pos_set[p];
     bool ok;
     if (s == -1)
       ok = t >= 0 && t < a.vocab;
     else
-      ok = in_set(a.set_ids + a.set_offsets[s], a.set_offsets[s + 1] - a.set_offsets[s], t);
+      ok = in_set(ids + a.set_offsets[s], a.set_offsets[s + 1] - a.set_offsets[s], t);
     if (!ok) first = min(first, p - 1);
     const int q = a.partner[p];
     if (q >= 0 && ((t == a.off_id) != (tok[q - 1] == a.off_id))) first = min(first, p - 1);
@@ -62,9 +81,14 @@ __global__ __launch_bounds__(64) void validate_kernel(ValidateArgs a) {
     }
   }
   first = wave_min(first);
-  if (lane == 0) {
-    a.first_out[b] = first == INT_MAX ? -1 : first;
-    a.k_out[b] = first == INT_MAX ? P : 0;
+  if ((tid & 63) == 0) red[tid >> 6] = first;
+  __syncthreads();
+  if (tid == 0) {
+    int f = red[0];
+#pragma unroll
+    for (int i = 1; i < kValThreads / 64; ++i) f = min(f, red[i]);
+    a.first_out[b] = f == INT_MAX ? -1 : f;
+    a.k_out[b] = f == INT_MAX ? P : 0;
   }
 }
 
@@ -94,7 +118,12 @@ __global__ __launch_bounds__(64) void verify_kernel(const int32_t* __restrict__ 
 hipError_t validate_primitive(const ValidateArgs& a, hipStream_t st) {
   ProfScope prof("validate", st);
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(validate_kernel, dim3(a.B), dim3(64), 0, st, a);
+  constexpr size_t kMaxLds = 64 * 1024;
+  const size_t tok_bytes = (size_t)(a.L - 1) * 4, id_bytes = (size_t)a.n_set_ids * 4;
+  const int stage_tok = tok_bytes <= kMaxLds;
+  const int stage_ids = (stage_tok ? tok_bytes : 0) + id_bytes <= kMaxLds;
+  const size_t lds = (stage_tok ? tok_bytes : 0) + (stage_ids ? id_bytes : 0);
+  hipLaunchKernelGGL(validate_kernel, dim3(a.B), dim3(kValThreads), lds, st, a, stage_tok, stage_ids);
   return hipGetLastError();
 }
 

@@ -209,7 +209,7 @@ int32_t fpd_drafter_create(const fpd_config* cfg, const fpd_weights* w, fpd_draf
   std::memset(&d->tab, 0, sizeof(d->tab));
   const int half = c.head_dim / 2;
   for (int i = 0; i < half; ++i)
-    d->tab.inv_freq[i] = (float)std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
+    d->tab.inv_rev[i] = std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim) / (2.0 * M_PI);
   *out = d;
   return FPD_OK;
 }
@@ -482,6 +482,7 @@ int32_t fpd_validate_primitive(const fpd_layout* lay, const int32_t* tokens, int
   const HostLayout& h = lay->host;
   ValidateArgs a{};
   a.tokens = tokens, a.pos_set = lay->pos_set, a.set_offsets = lay->set_offsets, a.set_ids = lay->set_ids;
+  a.n_set_ids = (int)h.set_ids.size();
   a.partner = lay->partner, a.field_w = lay->field_w;
   a.B = B, a.L = h.L, a.vocab = h.vocab, a.off_id = h.off_id, a.fill_id = h.fill_id, a.digit0_id = h.digit0_id;
   a.k_out = k_out, a.first_out = first_invalid_out;

@@ -96,6 +96,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
   u32x4_t rk[4], rv[4];
   auto gload = [&](int t) {
     const Src sr = src(t);
+    if (sr.key0 + KT <= sr.count) {  // full tile: no per-lane bounds
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sl = tid + i * 256;
+        const int kr = sl >> 4, kc = (sl & 15) ^ (kr & 15);
+        rk[i] = *(const u32x4_t*)(sr.k + (size_t)(sr.key0 + kr) * D + kc * 8);
+        const int dr = sl >> 3, vc = (sl & 7) ^ ((dr >> 1) & 7);
+        rv[i] = *(const u32x4_t*)(sr.v + (size_t)dr * sr.ldv + sr.key0 + vc * 8);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sl = tid + i * 256;
@@ -157,32 +168,31 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
         for (int kk = 0; kk < D / 16; ++kk)
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[kslot(krow, kk * 2 + lg)], qf[kk], s[kb], 0, 0, 0);
       }
-      // register r of sub-block kb holds key kb*32 + (r/8)*16 + lg*8 + r%8 for query lq
+      // register r of sub-block kb holds key kb*32 + (r/8)*16 + lg*8 + r%8 for query lq.
+      // The running max is kept in raw score units (scale > 0); exponents
+      // are fma(s, scale*log2(e), -m*scale*log2(e)).
       float mloc = -INFINITY;
       if (sr.key0 + KT <= sr.count) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[kb][r] *= p.scale_log2;
-            mloc = fmaxf(mloc, s[kb][r]);
-          }
+          for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kb][r]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = sr.key0 + kb * 32 + (r >> 3) * 16 + lg * 8 + (r & 7);
-            s[kb][r] = key < sr.count ? s[kb][r] * p.scale_log2 : -INFINITY;
+            s[kb][r] = key < sr.count ? s[kb][r] : -INFINITY;
             mloc = fmaxf(mloc, s[kb][r]);
           }
       }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       // keep the reference max unless it would let exponents exceed 2^kRescale
-      const bool grow = mloc > m_run + kRescale;
+      const bool grow = (mloc - m_run) * p.scale_log2 > kRescale;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? mloc : m_run;
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2) : 1.0f;
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -190,12 +200,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
           for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         m_run = m_new;
       }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run * p.scale_log2;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, neg_m));
           s[kb][r] = e;
           l_run += e;
         }
@@ -244,18 +254,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
         *(f32x4_t*)(dst + d0) = f32x4_t{o[dt][q4 * 4], o[dt][q4 * 4 + 1], o[dt][q4 * 4 + 2], o[dt][q4 * 4 + 3]};
       }
     if (lg == 0) {
-      p.mlpart[row * 2 + 0] = m_run;
+      p.mlpart[row * 2 + 0] = m_run * p.scale_log2;
       p.mlpart[row * 2 + 1] = l_tot;
     }
   }
 }
 
 // Merges split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, where
-// m_s is each split's reference max.  8 rows per workgroup, 4 dims per thread.
-template <class T>
+// m_s is each split's reference max (log2 units).  8 rows per workgroup, 4
+// dims per thread; the NS splits' loads are all issued before any use.
+template <class T, int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
-                                                           const float* __restrict__ ml, int splits,
-                                                           int B, int nq, int L, T* __restrict__ o) {
+                                                           const float* __restrict__ ml, int B, int nq, int L,
+                                                           T* __restrict__ o) {
   const size_t rows = (size_t)B * nq * L;
   const size_t row = (size_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   if (row >= rows) return;
@@ -263,17 +274,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int l = (int)(row % L);
   const size_t bh = row / L;
   const int head = (int)(bh % nq), b = (int)(bh / nq);
+  float ms[NS], ls[NS];
+  f32x4_t v[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const f32x2_t x = *(const f32x2_t*)(ml + (s * rows + row) * 2);
+    ms[s] = x[0];
+    ls[s] = x[1];
+    v[s] = *(const f32x4_t*)(opart + (s * rows + row) * D + d0);
+  }
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(s * rows + row) * 2]);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, ms[s]);
   float den = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const float ms = ml[(s * rows + row) * 2];
-    if (ms == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(ms - M);
-    den += w * ml[(s * rows + row) * 2 + 1];
-    const f32x4_t v = *(const f32x4_t*)(opart + (s * rows + row) * D + d0);
-    acc += w * v;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (ms[s] == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(ms[s] - M);
+    den += w * ls[s];
+    acc += w * v[s];
   }
   const float inv = 1.0f / den;
   T* dst = o + ((size_t)b * L + l) * (size_t)(nq * D) + (size_t)head * D + d0;
@@ -352,8 +372,10 @@ int attn_splits(int B, int L, int C, int nq, int nkv, int* q_tiles_out, int* tot
   const int q_tiles = (R + QROWS - 1) / QROWS;
   const int tiles = (C + KT - 1) / KT + (L + KT - 1) / KT;
   const int base = q_tiles * B * nkv;
+  // two workgroups fit on a CU: split the keys until the grid would exceed
+  // one pass over the 512 slots (more splits only add combine traffic)
   int splits = 1;
-  while (base * splits < 512 && splits * 2 <= tiles) splits *= 2;
+  while (base * splits * 2 <= 512 && splits * 2 <= tiles && splits < 32) splits *= 2;
   if (q_tiles_out) *q_tiles_out = q_tiles;
   if (total_tiles) *total_tiles = tiles;
   return splits;
@@ -399,8 +421,21 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     if (e != hipSuccess || p.splits == 1) return e;
     ProfScope prof("attn_combine", st);
     const size_t nrows = (size_t)a.B * a.nq * a.L;
-    hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3((unsigned)((nrows + 7) / 8)), dim3(256), 0, st,
-                       p.opart, p.mlpart, p.splits, a.B, a.nq, a.L, (bf16_t*)a.o);
+    const dim3 cg((unsigned)((nrows + 7) / 8));
+    switch (p.splits) {
+#define FPD_COMB(NS)                                                                                            \
+  case NS:                                                                                                      \
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, NS>), cg, dim3(256), 0, st, p.opart, p.mlpart, a.B, a.nq, a.L, \
+                       (bf16_t*)a.o);                                                                          \
+    break;
+      FPD_COMB(2)
+      FPD_COMB(4)
+      FPD_COMB(8)
+      FPD_COMB(16)
+      FPD_COMB(32)
+#undef FPD_COMB
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   const int rows = a.B * a.nq * a.L;

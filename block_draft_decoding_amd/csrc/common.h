@@ -11,6 +11,7 @@ typedef uint16_t bf16_t;  // raw IEEE bfloat16 bits
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -63,16 +64,21 @@ __device__ __forceinline__ bool arg_better(float v1, int c1, float v2, int c2) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Rotary embedding constants: inverse frequencies theta^(-2i/d) computed on
-// the host in double precision (d/2 <= 64 entries).
+// Rotary embedding constants: the rotation of pair i advances by
+// theta^(-2i/d) / (2 pi) turns per position, computed on the host in double
+// precision (d/2 <= 64 entries).
 struct RopeTab {
-  float inv_freq[64];
+  double inv_rev[64];
 };
 
-// Rotates the pair (x_i, x_{i + d/2}) by the angle pos * inv_freq[i].
-__device__ __forceinline__ void rope_pair(float& x0, float& x1, int pos, float inv) {
-  float s, c;
-  sincosf((float)pos * inv, &s, &c);
+// Rotates the pair (x_i, x_{i + d/2}) by pos * inv_rev turns.  The turn count
+// is reduced to [0, 1) in double precision (exact enough for any position
+// the int range allows) and the hardware sine/cosine, which take turns,
+// evaluate it.
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, int pos, double inv_rev) {
+  const double r = (double)pos * inv_rev;
+  const float t = (float)(r - floor(r));
+  const float s = __builtin_amdgcn_sinf(t), c = __builtin_amdgcn_cosf(t);
   const float y0 = x0 * c - x1 * s;
   const float y1 = x1 * c + x0 * s;
   x0 = y0;

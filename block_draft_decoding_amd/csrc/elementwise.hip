@@ -5,6 +5,8 @@
 #include "../../include/fpd.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace fpd {
 namespace {
 
@@ -81,7 +83,10 @@ __device__ __forceinline__ void store_norm4<float>(float* dst, f32x4_t v, float 
 // rows r = b*L + l with l >= 1 produce output, at row b*(L-1) + l - 1 (the
 // drafter's final norm over the masked positions).  H is a multiple of 64
 // and at most 4096 (the row stays in registers: 4 float4 per thread).
-template <class T>
+// NS > 0: exactly NS split-K partials, all loads issued before the sums
+// (a runtime-length loop would serialise one memory round trip per split);
+// NS = 0: `splits` partials in a loop.
+template <class T, int NS>
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict__ partial, int splits, int M, int H,
                                                          float* __restrict__ h, const T* __restrict__ g, float eps,
                                                          T* __restrict__ out, int final_L) {
@@ -105,8 +110,18 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
     if (k < n4) {
       f32x4_t x = hr[k];
       if (pr) {
-        f32x4_t acc = pr[k];
-        for (int s = 1; s < splits; ++s) acc += pr[s * pstride + k];
+        f32x4_t acc;
+        if constexpr (NS > 0) {
+          f32x4_t parts[NS];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) parts[s] = pr[s * pstride + k];
+          acc = parts[0];
+#pragma unroll
+          for (int s = 1; s < NS; ++s) acc += parts[s];
+        } else {
+          acc = pr[k];
+          for (int s = 1; s < splits; ++s) acc += pr[s * pstride + k];
+        }
         x += acc;
         hr[k] = x;
       }
@@ -216,12 +231,23 @@ hipError_t residual_norm(int dt, const float* partial, int splits, int M, int H,
   ProfScope prof("resid_norm", st);
   if (M == 0) return hipSuccess;
   const unsigned grid = (unsigned)M;
+  auto launch = [&](auto tag, auto ns) {
+    typedef decltype(tag) T;
+    hipLaunchKernelGGL((resid_norm_kernel<T, decltype(ns)::value>), dim3(grid), dim3(256), 0, st, partial, splits,
+                       M, H, h, (const T*)g, eps, (T*)out, final_L);
+  };
+  auto by_splits = [&](auto tag) {
+    const int ns = partial ? splits : 1;
+    if (ns == 1) launch(tag, std::integral_constant<int, 1>{});
+    else if (ns == 2) launch(tag, std::integral_constant<int, 2>{});
+    else if (ns == 4) launch(tag, std::integral_constant<int, 4>{});
+    else if (ns == 8) launch(tag, std::integral_constant<int, 8>{});
+    else launch(tag, std::integral_constant<int, 0>{});
+  };
   if (dt == FPD_DTYPE_BF16)
-    hipLaunchKernelGGL(resid_norm_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, partial, splits, M, H, h,
-                       (const bf16_t*)g, eps, (bf16_t*)out, final_L);
+    by_splits(bf16_t{});
   else
-    hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(grid), dim3(256), 0, st, partial, splits, M, H, h,
-                       (const float*)g, eps, (float*)out, final_L);
+    by_splits(float{});
   return hipGetLastError();
 }
 

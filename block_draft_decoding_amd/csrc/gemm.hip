@@ -59,7 +59,7 @@ struct EpiQkv {
     const int head = p / half, i = p % half;
     const int b = m / L, l = m - b * L;
     if (head < nq + nkv) {
-      if (rope) rope_pair(x0, x1, pos0 + l, tab.inv_freq[i]);
+      if (rope) rope_pair(x0, x1, pos0 + l, tab.inv_rev[i]);
       T* dst = head < nq ? q + (((size_t)b * nq + head) * L + l) * d
                          : k + (((size_t)b * nkv + (head - nq)) * L + l) * d;
       Elem<T>::st(dst + i, x0);
@@ -81,7 +81,7 @@ struct EpiCtx {
     const int head = p / half, i = p % half;
     const int b = m / C, c = m - b * C;
     if (head < nkv) {
-      if (rope) rope_pair(x0, x1, pos0 + c, tab.inv_freq[i]);
+      if (rope) rope_pair(x0, x1, pos0 + c, tab.inv_rev[i]);
       T* dst = k + (((size_t)b * nkv + head) * cap + c) * d;
       Elem<T>::st(dst + i, x0);
       Elem<T>::st(dst + i + half, x1);
@@ -410,6 +410,88 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// Split-K sum + RoPE + scatter for the q/k/v projection, one workgroup per
+// (32 rows, one head).  Partial columns of a head are contiguous, so the
+// reads coalesce; q/k rows are written d-contiguous, and v goes through an
+// LDS transpose so that its d-major rows are written position-contiguous.
+template <int NS>
+__global__ __launch_bounds__(256) void qkv_reduce_kernel(const float* __restrict__ partial, int M, int nw,
+                                                         EpiQkv<bf16_t> e) {
+  constexpr int RB = 32, HALF = 64, D = 128;  // rows per workgroup; bf16 heads are 128 wide
+  __shared__ float vt[D][RB + 1];
+  const int head = blockIdx.y, m0 = blockIdx.x * RB, tid = threadIdx.x;
+  const size_t stride = (size_t)M * nw;
+  const bool is_v = head >= e.nq + e.nkv;
+  const int i0 = (tid % 16) * 4;  // four consecutive rotation pairs per thread
+  const int rr = tid / 16;        // rows rr and rr + 16 of the block
+  f32x4_t x0[2], x1[2];
+  {
+    f32x4_t p0[2][NS], p1[2][NS];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int m = min(m0 + rr + 16 * k, M - 1);
+      const size_t o0 = (size_t)m * nw + (size_t)head * D + i0;
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp) {
+        p0[k][sp] = *(const f32x4_t*)(partial + sp * stride + o0);
+        p1[k][sp] = *(const f32x4_t*)(partial + sp * stride + o0 + HALF);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      x0[k] = p0[k][0];
+      x1[k] = p1[k][0];
+#pragma unroll
+      for (int sp = 1; sp < NS; ++sp) {
+        x0[k] += p0[k][sp];
+        x1[k] += p1[k][sp];
+      }
+    }
+  }
+  if (!is_v) {
+    const bool is_q = head < e.nq;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int m = m0 + rr + 16 * k;
+      if (m >= M) continue;
+      const int b = m / e.L, l = m - b * e.L;
+      if (e.rope) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float a0 = x0[k][c], a1 = x1[k][c];
+          rope_pair(a0, a1, e.pos0 + l, e.tab.inv_rev[i0 + c]);
+          x0[k][c] = a0;
+          x1[k][c] = a1;
+        }
+      }
+      bf16_t* dst = is_q ? e.q + (((size_t)b * e.nq + head) * e.L + l) * D
+                         : e.k + (((size_t)b * e.nkv + (head - e.nq)) * e.L + l) * D;
+      u32x2_t w0, w1;
+      w0[0] = pack_bf16x2(x0[k][0], x0[k][1]);
+      w0[1] = pack_bf16x2(x0[k][2], x0[k][3]);
+      w1[0] = pack_bf16x2(x1[k][0], x1[k][1]);
+      w1[1] = pack_bf16x2(x1[k][2], x1[k][3]);
+      *(u32x2_t*)(dst + i0) = w0;
+      *(u32x2_t*)(dst + i0 + HALF) = w1;
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      vt[i0 + c][rr + 16 * k] = x0[k][c];
+      vt[i0 + c + HALF][rr + 16 * k] = x1[k][c];
+    }
+  __syncthreads();
+  const int r = tid % RB;
+  const int m = m0 + r;
+  if (m >= M) return;
+  const int b = m / e.L, l = m - b * e.L;
+  bf16_t* dst = e.vt + ((size_t)b * e.nkv + (head - e.nq - e.nkv)) * D * e.Lp + l;
+  for (int dd = tid / RB; dd < D; dd += 256 / RB) dst[(size_t)dd * e.Lp] = f2bf(vt[dd][r]);
+}
+
 // ---- f32 SIMT kernel (the fp32 drafter) -----------------------------------------------
 template <bool PAIRED, class Map, class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int lda, int M,
@@ -634,8 +716,32 @@ hipError_t gemm_qkv(int dt, const void* A, int M, int K, const void* Wqkv, const
   if (dt == FPD_DTYPE_BF16) {
     EpiQkv<bf16_t> e{(bf16_t*)o.q, (bf16_t*)o.k, (bf16_t*)o.vt, o.L, o.Lp, o.nq, o.nkv, o.d, half,
                      o.pos0, o.rope, o.tab};
-    return run_bf16<true>(A, K, M, K, Wqkv, MapRope{half}, pairs, nw, e, partial, partial_bytes, st,
-                          "gemm_qkv");
+    GemmPlan pl = plan_gemm_bf16(M, pairs, K, nw, true);
+    if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) {
+      pl.splits = 1;
+      pl.partial_floats = 0;
+    }
+    hipError_t err = run_bf16_plan<true>(pl, A, K, M, K, Wqkv, MapRope{half}, pairs, nw, e, partial, st, "gemm_qkv",
+                                         /*reduce=*/false);
+    if (err != hipSuccess || pl.splits == 1 || M == 0) return err;
+    ProfScope prof("qkv_reduce", st);
+    const dim3 grid((M + 31) / 32, o.nq + 2 * o.nkv);
+    switch (pl.splits) {
+#define FPD_QKVR(NS)                                                                                  \
+  case NS:                                                                                            \
+    hipLaunchKernelGGL((qkv_reduce_kernel<NS>), grid, dim3(256), 0, st, partial, M, nw, e);         \
+    break;
+      FPD_QKVR(2)
+      FPD_QKVR(4)
+      FPD_QKVR(8)
+#undef FPD_QKVR
+      default: {
+        const size_t n = (size_t)M * pairs;
+        hipLaunchKernelGGL((splitk_reduce_kernel<true, MapRope, EpiQkv<bf16_t>>), dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), 0, st, partial, pl.splits, M, nw, pairs, MapRope{half}, e);
+      }
+    }
+    return hipGetLastError();
   }
   EpiQkv<float> e{(float*)o.q, (float*)o.k, (float*)o.vt, o.L, o.Lp, o.nq, o.nkv, o.d, half,
                   o.pos0, o.rope, o.tab};

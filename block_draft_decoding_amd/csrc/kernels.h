@@ -173,6 +173,7 @@ struct ValidateArgs {
   const int32_t* pos_set;    // [L]
   const int32_t* set_offsets;
   const int32_t* set_ids;
+  int n_set_ids;
   const int32_t* partner;    // [L]
   const int32_t* field_w;    // [L]: width at a field's first digit position, else 0
   int B, L, vocab, off_id, fill_id, digit0_id;
