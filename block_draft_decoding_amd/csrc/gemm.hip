@@ -16,6 +16,7 @@
 
 #include "../../include/fpd.h"
 #include "kernels.h"
+#include "lds_pipe.h"
 
 namespace fpd {
 
@@ -102,17 +103,6 @@ struct EpiGlu {
   }
 };
 
-// ---- bf16 MFMA kernel ---------------------------------------------------------
-// Operand tiles go global -> LDS directly (global_load_lds_dwordx4: lane i of
-// a wave instruction fills 16-byte slot base + i) through a STAGES-deep ring,
-// so several K-tiles are in flight per workgroup without register staging.
-// A tile row (BK bf16 = CH chunks of 16 bytes) keeps chunk c at position
-// c ^ ((row / (16 / CH)) % CH): the MFMA operand reads (16 rows x 16 bytes
-// per LDS cycle) then hit distinct banks.  The swizzle is applied by choosing which
-// global chunk each lane loads.  Lanes whose row lies outside the problem
-// load a clamped in-range row instead of being switched off, so every wave
-// issues the same number of loads per stage and vmcnt counts stay exact; the
-// outputs of those rows/columns are never stored.
 // Maps the launch index to a tile (row tile fastest, then column tile, then
 // K split).  Each XCD runs one contiguous range of tiles (workgroups are
 // dispatched to XCDs round-robin), so the row tiles that share a weight tile
@@ -135,52 +125,18 @@ __device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, i
   return (s - h0 + local - (h1 - h0)) * m_tiles + m_full;
 }
 
-// One 16-byte buffer load per lane written straight into LDS: lane i fills
-// the 16 bytes at dst + 16 i (dst is wave-uniform).  Only the device pass
-// sees the builtin; the host pass would otherwise drop the kernel stubs.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, u32x4_t* dst, uint32_t voff, int soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
-#endif
-}
-
-template <int CH>  // 16-byte chunks per row (BK / 8)
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * CH + (c ^ ((r / (16 / CH)) & (CH - 1)));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads(): that fence
-// makes the compiler wait for every outstanding load (vmcnt(0)), which would
-// drain the stages in flight.  LDS hand-over is ordered by the explicit
-// vmcnt wait before it; the clobber keeps LDS accesses from moving across.
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-
-// s_waitcnt lgkmcnt(0) (vmcnt and expcnt fields at their maximum), issued
-// as the builtin so that the compiler's own wait insertion sees it: scalar
-// loads still pending make it treat the LDS counter as out of order and
-// fall back to full waits before every MFMA group.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Waits until at most `ahead` later stages (LPS loads each) are outstanding.
-template <int LPS, int MAXA>
-__device__ __forceinline__ void wait_stages(int ahead) {
-  if constexpr (MAXA > 0) {
-    if (ahead >= MAXA) {
-      wait_vmcnt<LPS * MAXA>();
-      return;
-    }
-    wait_stages<LPS, MAXA - 1>(ahead);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
+// ---- bf16 MFMA kernel ---------------------------------------------------------
+// Operand tiles go global -> LDS directly (an LDS-writing buffer load: lane i
+// of a wave instruction fills 16-byte slot base + i) through a STAGES-deep
+// ring, so several K-tiles are in flight per workgroup without register
+// staging.
+// A tile row (BK bf16 = CH chunks of 16 bytes) keeps chunk c at position
+// c ^ ((row / (16 / CH)) % CH): the MFMA operand reads (16 rows x 16 bytes
+// per LDS cycle) then hit distinct banks.  The swizzle is applied by choosing which
+// global chunk each lane loads.  Lanes whose row lies outside the problem
+// load a clamped in-range row instead of being switched off, so every wave
+// issues the same number of loads per stage and vmcnt counts stay exact; the
+// outputs of those rows/columns are never stored.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool PAIRED, class Map, class Epi>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, int w_rows, Map map,
@@ -577,6 +533,8 @@ hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int 
                          bool reduce = true) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   if (grid == 0) return hipSuccess;
+  // buffer descriptors address at most 4 GiB per operand
+  if ((size_t)M * lda * 2 > 0xffffffffull || (size_t)nw * K * 2 > 0xffffffffull) return hipErrorInvalidValue;
   const bf16_t* a = (const bf16_t*)A;
   const bf16_t* w = (const bf16_t*)W;
   float* part = pl.splits > 1 ? partial : nullptr;

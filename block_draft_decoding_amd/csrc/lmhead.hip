@@ -11,14 +11,15 @@
 
 #include "../../include/fpd.h"
 #include "kernels.h"
+#include "lds_pipe.h"
 
 namespace fpd {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDSW = BK + 8;
 constexpr int HBM = 32;    // rows per tile (bf16)
 constexpr int HBN = 128;   // columns per chunk (bf16): 4 waves x 32
+constexpr int HST = 4;     // depth of the global -> LDS ring (bf16)
 constexpr int FBM = 16;    // f32 path: rows per tile
 constexpr int FBN = 64;    // f32 path: columns per chunk
 
@@ -53,65 +54,88 @@ __device__ __forceinline__ void wave_argmax(float& v, int& c, int width) {
   }
 }
 
+// bf16 path: the hidden rows of the set's positions and the set's gathered
+// W_lm rows stream global -> LDS through an HST-deep ring of LDS-writing
+// buffer loads (K-tile offsets are scalar; each lane's row offset is fixed),
+// so several K-tiles are in flight while the MFMAs run.  16-byte chunks are
+// bank-swizzled as in the dense GEMM.
 __global__ __launch_bounds__(256) void head_bf16_kernel(HeadArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][HBM * LDSW];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][HBN * LDSW];
+  constexpr int CH = BK / 8;                       // 16-byte chunks per tile row
+  constexpr int STAGE = (HBM + HBN) * CH;          // chunks per stage
+  constexpr int BI = HBN * CH / 256;               // B loads per thread and stage (A: one)
+  constexpr int LPS = 1 + BI;
+  __shared__ u32x4_t lds[HST * STAGE];
   __shared__ float red_v[4][HBM];
   __shared__ int red_c[4][HBM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int rowmap[HBM];  // hidden / output row of each tile row (rows past the set repeat a valid one)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, lg = lane >> 5;
   const Item it = find_item(a, xcd_remap(blockIdx.x, gridDim.x), HBM);
   if (it.set < 0) return;
   const HeadSet& S = a.sets[it.set];
   const int M = a.B * S.n_pos, H = a.H;
   const int m0 = it.mt * HBM, c0 = it.chunk * HBN;
-  const bf16_t* hid = (const bf16_t*)a.hidden;
-  const bf16_t* W = (const bf16_t*)S.w;
 
-  // one A chunk and four B chunks (16 bytes each) per thread and K-tile
-  const int arow = tid >> 3, akc = (tid & 7) * 8;
-  const bf16_t* aptr = (m0 + arow < M) ? hid + (size_t)set_row(a, S, m0 + arow) * H : nullptr;
-  const bf16_t* bptr[4];
-  int blds[4], bkc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + i * 256, row = c >> 3;
-    bkc[i] = (c & 7) * 8;
-    blds[i] = row * LDSW + bkc[i];
-    bptr[i] = (c0 + row < S.n_cols) ? W + (size_t)(c0 + row) * H : nullptr;
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.hidden, (short)0, (int)((size_t)a.B * (a.L - 1) * H * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)S.w, (short)0, (int)((size_t)S.n_cols * H * 2), 0x00020000);
+  if (tid < HBM) rowmap[tid] = set_row(a, S, min(m0 + tid, M - 1));
+  uint32_t aoff, boff[BI];
+  {
+    const int sl = wave * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
+    const int row = set_row(a, S, min(m0 + r, M - 1));
+    aoff = (uint32_t)(((size_t)row * H + c * 8) * 2);
   }
-  u32x4_t ra, rb[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-    ra = aptr ? *(const u32x4_t*)(aptr + k0 + akc) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rb[i] = bptr[i] ? __builtin_nontemporal_load((const u32x4_t*)(bptr[i] + k0 + bkc[i]))
-                      : u32x4_t{0, 0, 0, 0};
-  };
-  auto sstore = [&](int buf) {
-    *(u32x4_t*)&As[buf][arow * LDSW + akc] = ra;
+  for (int i = 0; i < BI; ++i) {
+    const int sl = (wave * BI + i) * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
+    const int col = min(c0 + r, S.n_cols - 1);
+    boff[i] = (uint32_t)(((size_t)col * H + c * 8) * 2);
+  }
+  auto issue = [&](int kt, int stage) {
+    const int soff = kt * BK * 2;
+    u32x4_t* base = lds + stage * STAGE;
+    lds_dma16(arsrc, base + wave * 64, aoff, soff);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)&Bs[buf][blds[i]] = rb[i];
+    for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + HBM * CH + (wave * BI + i) * 64, boff[i], soff);
   };
+
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const int KT = H / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < HST; ++s)
+    if (s < KT) issue(s, s);
+  bf16x8_t af[2], bfv[2];
+  auto fetch = [&](int stage, int kk, int buf) {
+    const u32x4_t* As = lds + stage * STAGE;
+    af[buf] = __builtin_bit_cast(bf16x8_t, As[swz<CH>(lq, kk * 2 + lg)]);
+    bfv[buf] = __builtin_bit_cast(bf16x8_t, As[HBM * CH + swz<CH>(wave * 32 + lq, kk * 2 + lg)]);
+  };
+  wait_lgkm0();
+  wait_stages<LPS, HST - 1>(min(HST - 1, KT - 1));
+  barrier_nofence();
+  fetch(0, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+    const int stage = kt % HST;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const bf16x8_t af = *(const bf16x8_t*)&As[cur][lq * LDSW + kk * 16 + lg * 8];
-      const bf16x8_t bfv = *(const bf16x8_t*)&Bs[cur][(wave * 32 + lq) * LDSW + kk * 16 + lg * 8];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfv, acc, 0, 0, 0);
+      if (kk + 1 < BK / 16) {
+        fetch(stage, kk + 1, (kk + 1) & 1);
+      } else {
+        wait_lgkm0();
+        if (kt + 1 < KT) wait_stages<LPS, HST - 2>(min(HST - 2, KT - 2 - kt));
+        barrier_nofence();
+        if (kt + HST < KT) issue(kt + HST, stage);
+        if (kt + 1 < KT) fetch((kt + 1) % HST, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1], bfv[kk & 1], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
   }
 
   // epilogue: this lane holds column n of rows rr(r)
@@ -123,7 +147,7 @@ __global__ __launch_bounds__(256) void head_bf16_kernel(HeadArgs a) {
     const int m = m0 + rr;
     const float v = acc[r];
     if (m < M && ncol) {
-      const int grow = set_row(a, S, m);
+      const int grow = rowmap[rr];
       if (a.logits) a.logits[(size_t)grow * a.width + n] = v;
       if (n == S.off_col) a.offv[grow] = v;
     }
@@ -150,7 +174,7 @@ __global__ __launch_bounds__(256) void head_bf16_kernel(HeadArgs a) {
       }
     const int m = m0 + tid;
     if (m < M) {
-      const size_t slot = (size_t)set_row(a, S, m) * a.max_chunks + S.part_base + it.chunk;
+      const size_t slot = (size_t)rowmap[tid] * a.max_chunks + S.part_base + it.chunk;
       a.pval[slot] = bv;
       a.pcol[slot] = bc;
     }
@@ -214,17 +238,30 @@ __global__ __launch_bounds__(256) void head_f32_kernel(HeadArgs a) {
   }
 }
 
+// Best (value, column) of a row's chunk partials.  Loads go in batches of 8
+// issued before the comparisons, so a row costs one memory round trip per
+// 8 chunks rather than one per chunk.
 __device__ __forceinline__ void best_of_row(const ReduceArgs& a, int row, int slot, float& v, int& c) {
   v = -INFINITY;
   c = INT_MAX;
   const int nc = a.set_chunks[slot];
-  for (int k = 0; k < nc; ++k) {
-    const float v2 = a.pval[(size_t)row * a.max_chunks + k];
-    const int c2 = a.pcol[(size_t)row * a.max_chunks + k];
-    if (arg_better(v2, c2, v, c)) {
-      v = v2;
-      c = c2;
+  const float* pv = a.pval + (size_t)row * a.max_chunks;
+  const int32_t* pc = a.pcol + (size_t)row * a.max_chunks;
+  for (int k0 = 0; k0 < nc; k0 += 8) {
+    float v8[8];
+    int c8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok = k0 + k < nc;
+      v8[k] = ok ? pv[k0 + k] : -INFINITY;
+      c8[k] = ok ? pc[k0 + k] : INT_MAX;
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (arg_better(v8[k], c8[k], v, c)) {
+        v = v8[k];
+        c = c8[k];
+      }
   }
 }
 
@@ -291,6 +328,10 @@ hipError_t lm_head_partials(int dt, const HeadArgs& a, hipStream_t st) {
   for (int s = 0; s < a.n_sets; ++s)
     items += (long)((a.B * a.sets[s].n_pos + bm - 1) / bm) * a.sets[s].n_chunks;
   if (items == 0) return hipSuccess;
+  // buffer descriptors address at most 4 GiB per operand
+  if ((size_t)a.B * (a.L - 1) * a.H * 2 > 0xffffffffull) return hipErrorInvalidValue;
+  for (int s = 0; s < a.n_sets; ++s)
+    if ((size_t)a.sets[s].n_cols * a.H * 2 > 0xffffffffull) return hipErrorInvalidValue;
   if (dt == FPD_DTYPE_BF16)
     hipLaunchKernelGGL(head_bf16_kernel, dim3((unsigned)items), dim3(256), 0, st, a);
   else
