@@ -19,13 +19,20 @@
 
 #include "../../include/fpd.h"
 #include "kernels.h"
+#include "lds_pipe.h"
 
 namespace fpd {
 namespace {
 
 constexpr int KT = 64;          // keys per tile
 constexpr int D = 128;          // head dim of the bf16 path
-constexpr int QROWS = 128;      // packed query rows per workgroup (4 waves x 32)
+constexpr int AW = 8;           // waves per workgroup
+constexpr int QROWS = AW * 32;  // packed query rows per workgroup
+constexpr int AST = 3;          // depth of the global -> LDS ring
+constexpr int KSLOTS = KT * 16; // 16-byte chunks of a K tile (64 keys x 256 bytes)
+constexpr int VSLOTS = D * 8;   // 16-byte chunks of a V^T tile (128 dims x 64 keys)
+constexpr int ASTAGE = KSLOTS + VSLOTS;
+constexpr int APT = KSLOTS / (AW * 64);  // K (and V) loads per thread and stage
 constexpr float kRescale = 8.0f;  // lazy rescale: keep the running max until it grows by 2^8
 
 struct AttnP {
@@ -45,11 +52,17 @@ __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1)
 __device__ __forceinline__ int kslot(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 __device__ __forceinline__ int vslot(int d, int c) { return d * 8 + (c ^ ((d >> 1) & 7)); }
 
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
-  __shared__ u32x4_t Ks[2][KT * 16];
-  __shared__ u32x4_t Vs[2][D * 8];
+// K and V^T tiles stream global -> LDS through an AST-deep ring of
+// LDS-writing buffer loads (one descriptor per source segment; per-lane
+// offsets are fixed, the tile's key offset is scalar).  Keys past a
+// segment's valid count are masked out of the scores; in the (at most two)
+// partial tiles of a workgroup their V^T columns are zeroed in LDS before
+// use, so padding memory never reaches the P V product.
+__global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
+  __shared__ u32x4_t lds[AST * ASTAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = tile % p.q_tiles;
   const int rest = tile / p.q_tiles;
@@ -73,69 +86,37 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
   const int t0 = (int)((long)sp * total / p.splits), t1 = (int)((long)(sp + 1) * total / p.splits);
   const size_t bhk = (size_t)b * p.nkv + j;
 
-  struct Src {
-    const bf16_t *k, *v;
-    int ldv, key0, count;
-  };
-  auto src = [&](int t) {
-    Src r;
-    if (t < p.ctx_tiles) {
-      r.key0 = t * KT, r.count = p.C, r.ldv = p.cap;
-      r.k = p.ck + bhk * p.cap * D;
-      r.v = p.cvt + bhk * D * p.cap;
-    } else {
-      r.key0 = (t - p.ctx_tiles) * KT, r.count = p.L, r.ldv = p.Lp;
-      r.k = p.kb + bhk * p.L * D;
-      r.v = p.vbt + bhk * D * p.Lp;
-    }
-    return r;
-  };
-
-  // staging: thread handles LDS slots tid + i*256 of each tile; the global
-  // chunk it loads is chosen so that the swizzled layout comes out directly
-  u32x4_t rk[4], rv[4];
-  auto gload = [&](int t) {
-    const Src sr = src(t);
-    if (sr.key0 + KT <= sr.count) {  // full tile: no per-lane bounds
+  const __amdgpu_buffer_rsrc_t kc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ck + bhk * p.cap * D), (short)0, (int)((size_t)p.cap * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t kbk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.kb + bhk * p.L * D), (short)0, (int)((size_t)p.L * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.cvt + bhk * D * p.cap), (short)0, (int)((size_t)D * p.cap * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vbk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.vbt + bhk * D * p.Lp), (short)0, (int)((size_t)D * p.Lp * 2), 0x00020000);
+  // per-lane source offsets of the slots this lane fills (the swizzle is
+  // applied by choosing which global chunk lands in which slot)
+  uint32_t koff[APT], voff_c[APT], voff_b[APT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sl = tid + i * 256;
-        const int kr = sl >> 4, kc = (sl & 15) ^ (kr & 15);
-        rk[i] = *(const u32x4_t*)(sr.k + (size_t)(sr.key0 + kr) * D + kc * 8);
-        const int dr = sl >> 3, vc = (sl & 7) ^ ((dr >> 1) & 7);
-        rv[i] = *(const u32x4_t*)(sr.v + (size_t)dr * sr.ldv + sr.key0 + vc * 8);
-      }
-      return;
-    }
+  for (int i = 0; i < APT; ++i) {
+    const int sl = (wave * APT + i) * 64 + lane;
+    const int kr = sl >> 4, kc_ = (sl & 15) ^ (kr & 15);
+    koff[i] = (uint32_t)((kr * D + kc_ * 8) * 2);
+    const int dr = sl >> 3, vc_ = (sl & 7) ^ ((dr >> 1) & 7);
+    voff_c[i] = (uint32_t)(((size_t)dr * p.cap + vc_ * 8) * 2);
+    voff_b[i] = (uint32_t)(((size_t)dr * p.Lp + vc_ * 8) * 2);
+  }
+  auto tile_key0 = [&](int t) { return t < p.ctx_tiles ? t * KT : (t - p.ctx_tiles) * KT; };
+  auto tile_count = [&](int t) { return t < p.ctx_tiles ? p.C : p.L; };
+  auto issue = [&](int t, int stage) {
+    const bool ctx = t < p.ctx_tiles;
+    const int key0 = tile_key0(t);
+    u32x4_t* base = lds + stage * ASTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sl = tid + i * 256;
-      const int kr = sl >> 4, kc = (sl & 15) ^ (kr & 15);
-      rk[i] = (sr.key0 + kr < sr.count) ? *(const u32x4_t*)(sr.k + (size_t)(sr.key0 + kr) * D + kc * 8)
-                                        : u32x4_t{0, 0, 0, 0};
-      const int dr = sl >> 3, vc = (sl & 7) ^ ((dr >> 1) & 7);
-      const int kabs = sr.key0 + vc * 8;
-      u32x4_t v = u32x4_t{0, 0, 0, 0};
-      if (kabs < sr.count) {
-        v = *(const u32x4_t*)(sr.v + (size_t)dr * sr.ldv + kabs);
-        const int nvalid = sr.count - kabs;  // keys past the valid count become exact zeros
-        if (nvalid < 8) {
+    for (int i = 0; i < APT; ++i) lds_dma16(ctx ? kc : kbk, base + (wave * APT + i) * 64, koff[i], key0 * D * 2);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (2 * e >= nvalid) v[e] = 0;
-            else if (2 * e + 1 >= nvalid) v[e] &= 0xffffu;
-          }
-        }
-      }
-      rv[i] = v;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Ks[buf][tid + i * 256] = rk[i];
-      Vs[buf][tid + i * 256] = rv[i];
-    }
+    for (int i = 0; i < APT; ++i)
+      lds_dma16(ctx ? vc : vbk, base + KSLOTS + (wave * APT + i) * 64, ctx ? voff_c[i] : voff_b[i], key0 * 2);
   };
 
   f32x16_t o[D / 32];
@@ -146,18 +127,39 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
   float m_run = -INFINITY, l_run = 0.f;
   const int krow0 = swap23(lq);
 
-  if (t0 < t1) {
-    gload(t0);
-    sstore(0);
-    __syncthreads();
-  }
+#pragma unroll
+  for (int s2 = 0; s2 < AST - 1; ++s2)
+    if (t0 + s2 < t1) issue(t0 + s2, s2);
+  wait_lgkm0();
+
   for (int t = t0; t < t1; ++t) {
-    const int cur = (t - t0) & 1;
-    const Src sr = src(t);
-    if (t + 1 < t1) gload(t + 1);
+    const int stage = (t - t0) % AST;
+    const int key0 = tile_key0(t), count = tile_count(t);
+    wait_stages<2 * APT, AST - 2>(min(AST - 2, t1 - 1 - t));
+    barrier_nofence();  // tile t landed for every wave; stage of tile t-1 is free
+    u32x4_t* Ks = lds + stage * ASTAGE;
+    u32x4_t* Vs = Ks + KSLOTS;
+    if (key0 + KT > count) {  // partial tile: zero the V^T columns of keys past the count
+      for (int sl = tid; sl < VSLOTS; sl += AW * 64) {
+        const int dr = sl >> 3, c = (sl & 7) ^ ((dr >> 1) & 7);
+        const int nvalid = count - (key0 + c * 8);
+        if (nvalid < 8) {
+          u32x4_t v = Vs[sl];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (2 * e >= nvalid) v[e] = 0;
+            else if (2 * e + 1 >= nvalid) v[e] &= 0xffffu;
+          }
+          Vs[sl] = v;
+        }
+      }
+      wait_lgkm0();
+      barrier_nofence();
+    }
+    if (t + AST - 1 < t1) issue(t + AST - 1, (t - t0 + AST - 1) % AST);
     if (wave_active) {
-      const bf16x8_t* Kb = (const bf16x8_t*)Ks[cur];
-      const bf16x8_t* Vb = (const bf16x8_t*)Vs[cur];
+      const bf16x8_t* Kb = (const bf16x8_t*)Ks;
+      const bf16x8_t* Vb = (const bf16x8_t*)Vs;
       f32x16_t s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
       // The running max is kept in raw score units (scale > 0); exponents
       // are fma(s, scale*log2(e), -m*scale*log2(e)).
       float mloc = -INFINITY;
-      if (sr.key0 + KT <= sr.count) {
+      if (key0 + KT <= count) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -182,8 +184,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = sr.key0 + kb * 32 + (r >> 3) * 16 + lg * 8 + (r & 7);
-            s[kb][r] = key < sr.count ? s[kb][r] : -INFINITY;
+            const int key = key0 + kb * 32 + (r >> 3) * 16 + lg * 8 + (r & 7);
+            s[kb][r] = key < count ? s[kb][r] : -INFINITY;
             mloc = fmaxf(mloc, s[kb][r]);
           }
       }
@@ -222,8 +224,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
                                                             o[dt], 0, 0, 0);
         }
     }
-    if (t + 1 < t1) sstore(cur ^ 1);
-    __syncthreads();
   }
 
   if (!qvalid) return;
@@ -372,10 +372,10 @@ int attn_splits(int B, int L, int C, int nq, int nkv, int* q_tiles_out, int* tot
   const int q_tiles = (R + QROWS - 1) / QROWS;
   const int tiles = (C + KT - 1) / KT + (L + KT - 1) / KT;
   const int base = q_tiles * B * nkv;
-  // two workgroups fit on a CU: split the keys until the grid would exceed
-  // one pass over the 512 slots (more splits only add combine traffic)
+  // one workgroup per CU: split the keys until the grid would exceed one
+  // pass over the 256 CUs (more splits only add combine traffic)
   int splits = 1;
-  while (base * splits * 2 <= 512 && splits * 2 <= tiles && splits < 32) splits *= 2;
+  while (base * splits * 2 <= 256 && splits * 2 <= tiles && splits < 32) splits *= 2;
   if (q_tiles_out) *q_tiles_out = q_tiles;
   if (total_tiles) *total_tiles = tiles;
   return splits;
@@ -415,7 +415,7 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     const int grid = p.q_tiles * p.splits * a.B * a.nkv;
     {
       ProfScope prof("attention", st);
-      hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(256), 0, st, p);
+      hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(AW * 64), 0, st, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
