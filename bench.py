@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--workload", default="traj2d3d")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bounded sample)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 256 MiB device buffer 5 times (reference for the FETCH_SIZE / WRITE_SIZE "
+                         "counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -104,7 +107,17 @@ def main():
 
     import numpy as np
     import torch
-    from block_draft_decoding_amd import fpd, synth
+    from block_draft_decoding_amd import fpd, profiling, synth
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     s = wl.shape
@@ -206,6 +219,7 @@ def main():
             ach = nbytes / (avg_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+        roof["traffic"] = profiling.read_traffic(dom)
         roof.update({"kernel": dom, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": kern[dom][0] // nprof,
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
     kernels = {t: {"launches_per_step": round(c[0] / nprof, 2), "ms_per_step": round(c[1] / nprof, 4)}

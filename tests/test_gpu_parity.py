@@ -297,3 +297,61 @@ def test_full_size_points3d_sampled():
         rel_close(ck[:, b, c], kk[:, 0, 0], "bf16", f"ctx_k row {b},{c}")
         rel_close(cv[:, b, c], vv[:, 0, 0], "bf16", f"ctx_v row {b},{c}")
     progress(f"[full points3d] valid requests {int((ko > 0).sum())} of {wl.batch}")
+
+
+def test_padding_memory_never_reaches_outputs():
+    """Context capacity past the valid keys and every workspace byte hold NaN
+    before the calls.  Padding keys are masked out of the scores and their
+    value columns are zeroed before the P V product, and every workspace
+    buffer is written before it is read, so the outputs still match the
+    oracle."""
+    from block_draft_decoding_amd import fpd
+    wl = small_workload("traj2d3d", 2, 300, seed=64, n_points=7, off_id=4099 - 1020 + 1002)
+    inp = synth.make_inputs(wl)
+    g = GpuCase(wl, inp)
+    cap = 456                      # 156 keys of NaN capacity past C = 300 (not a tile multiple)
+    g.cap = cap
+    g.ws = fpd.alloc_workspace(g.d, g.B, cap, g.L)
+    g.ctx_k, g.ctx_v = fpd.alloc_context(g.d, g.B, cap)
+    g.ctx_k.fill_(float("nan"))
+    g.ctx_v.fill_(float("nan"))
+    g.ws.fill_(255)                # all-ones bytes: NaN in every float and bf16 view
+    g.fuse()
+    g.draft()
+    lg = g.argmax(logits=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(g.hidden.float()).all()
+    res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
+    compare_all(wl, g, lg, res, "bf16", "NaN padding")
+
+
+def test_validator_large_sets_from_global_memory():
+    """Legal-id sets too large to stage in LDS are searched in global memory;
+    results must stay bit-exact with the oracle."""
+    from block_draft_decoding_amd import fpd
+    V = 70_000
+    shape = replace(SMALL, vocab=V, n_layers=1)
+    rng = np.random.default_rng(11)
+    sets = [sorted(rng.choice(V - 8, 20_000, replace=False).tolist()) for _ in range(3)]
+    L = 41
+    pos_set = [-2] + [int(rng.integers(-1, 3)) for _ in range(L - 1)]
+    schema = dict(kind="custom", block_len=L, sets=sets, pos_set=pos_set, pairs=[], fields=[], off_id=-1,
+                  fill_id=-1, digit0_id=-1, coord_base=0, coord_count=0, start_id=V - 4, mask_id=V - 1,
+                  delim_id=-1, plus_id=-1, minus_id=-1)
+    w = fpd.weights_to_device(synth.make_weights(shape, seed=12), torch.bfloat16)
+    d = fpd.fpd_drafter_create(fpd.make_config(shape), w)
+    lay_d = fpd.fpd_layout_create(d, schema)
+    lay = O.build_layout(schema, V)
+    B = 256
+    toks = np.empty((B, L - 1), np.int32)
+    for p in range(1, L):
+        ids = lay.legal(p)
+        toks[:, p - 1] = ids[rng.integers(0, len(ids), size=B)]
+    for b in range(0, B, 2):       # foreign and out-of-vocabulary ids in half the rows
+        toks[b, rng.integers(0, L - 1)] = rng.choice([V - 5, -1, V + 3, int(rng.integers(0, V))])
+    k = torch.empty(B, dtype=torch.int32, device="cuda")
+    f = torch.empty_like(k)
+    fpd.fpd_validate_primitive(lay_d, torch.from_numpy(toks).cuda(), k, f)
+    ko, fo = O.validate_primitive(toks, lay)
+    assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
+    assert 0 < int((ko == 0).sum()) < B
