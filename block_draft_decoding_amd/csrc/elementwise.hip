@@ -237,12 +237,17 @@ hipError_t residual_norm(int dt, const float* partial, int splits, int M, int H,
                        M, H, h, (const T*)g, eps, (T*)out, final_L);
   };
   auto by_splits = [&](auto tag) {
-    const int ns = partial ? splits : 1;
-    if (ns == 1) launch(tag, std::integral_constant<int, 1>{});
-    else if (ns == 2) launch(tag, std::integral_constant<int, 2>{});
-    else if (ns == 4) launch(tag, std::integral_constant<int, 4>{});
-    else if (ns == 8) launch(tag, std::integral_constant<int, 8>{});
-    else launch(tag, std::integral_constant<int, 0>{});
+    switch (partial ? splits : 1) {
+      case 1: launch(tag, std::integral_constant<int, 1>{}); break;
+      case 2: launch(tag, std::integral_constant<int, 2>{}); break;
+      case 3: launch(tag, std::integral_constant<int, 3>{}); break;
+      case 4: launch(tag, std::integral_constant<int, 4>{}); break;
+      case 5: launch(tag, std::integral_constant<int, 5>{}); break;
+      case 6: launch(tag, std::integral_constant<int, 6>{}); break;
+      case 7: launch(tag, std::integral_constant<int, 7>{}); break;
+      case 8: launch(tag, std::integral_constant<int, 8>{}); break;
+      default: launch(tag, std::integral_constant<int, 0>{});
+    }
   };
   if (dt == FPD_DTYPE_BF16)
     by_splits(bf16_t{});

@@ -609,10 +609,13 @@ GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int sp
 }
 
 // Tile and split choice, from measured sweeps on MI355X (block rows M = 16,
-// 25 and 385 of the 2560-wide drafter, weights streamed from HBM): small M
-// streams the weights with many split-K workgroups; larger M takes the
-// 128x256 eight-wave tile when it alone nearly fills 256 CUs, else the same
-// tile split along K (deep K or paired outputs) or 64x128 tiles split along K.
+// 25 and 385 of the 2560-wide drafter, weights streamed from HBM, splits
+// 1..8): small M streams the weights with many split-K workgroups; larger M
+// takes the 128x256 eight-wave tile (one workgroup per CU) when it alone
+// nearly fills 256 CUs; deep-K or paired outputs split that tile along K so
+// that the row tiles (a partly filled last one counts its share of 32-row
+// blocks) cover about 80% of the CUs once; narrow plain outputs take 64x128 tiles
+// split along K.
 GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   const int kt = K / 64;
   auto with_splits = [&](int cfg, int lo, int hi) {
@@ -626,7 +629,12 @@ GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   if (M <= 64) return with_splits(GEMM_64x128_S3, 1024, 2048);
   const GemmPlan big = make_plan(GEMM_128x256_W8_S3, M, ncols, K, nw, paired, 1);
   if (big.m_tiles * big.n_tiles >= 224) return big;
-  if (paired || K >= 8192) return with_splits(GEMM_128x256_W8_S3, 160, 400);
+  if (paired || K >= 8192) {
+    const int full = M / 128, rem_blocks = (M - full * 128 + 31) / 32;  // 32-row blocks of the last tile
+    const double units = big.n_tiles * (full + 0.25 * rem_blocks);
+    const int s = std::max(1, std::min({8, (int)(0.8 * 256 / units), kt / 2}));
+    return make_plan(GEMM_128x256_W8_S3, M, ncols, K, nw, paired, s);
+  }
   return with_splits(GEMM_64x128_S3, 256, 640);
 }
 
@@ -690,7 +698,11 @@ hipError_t gemm_qkv(int dt, const void* A, int M, int K, const void* Wqkv, const
     hipLaunchKernelGGL((qkv_reduce_kernel<NS>), grid, dim3(256), 0, st, partial, M, nw, e);         \
     break;
       FPD_QKVR(2)
+      FPD_QKVR(3)
       FPD_QKVR(4)
+      FPD_QKVR(5)
+      FPD_QKVR(6)
+      FPD_QKVR(7)
       FPD_QKVR(8)
 #undef FPD_QKVR
       default: {
