@@ -199,8 +199,11 @@ int32_t fpd_workspace_size(const fpd_drafter *d, int32_t B, int32_t C, int32_t L
  *   Zn = RMSNorm(Z; g_fc), and for every drafter layer l:
  *   K_c = RoPE(Zn Wk_l^T) at positions pos0 .. pos0 + C - 1, V_c = Zn Wv_l^T,
  * where Wk_l / Wv_l are the K / V rows of layer l's w_qkv.
- * Writes rows 0..C-1 of ctx_k and ctx_v, each [n_layers, B, n_kv, ctx_cap, d]
- * DT (head-major; keys stored after RoPE).  ctx_cap >= C.                 */
+ * Writes keys 0..C-1 of ctx_k [n_layers, B, n_kv, ctx_cap, d] DT (keys
+ * stored after RoPE) and of ctx_v [n_layers, B, n_kv, d, ctx_cap] DT (values
+ * stored d-major, so attention reads them along keys).  ctx_cap >= C and a
+ * multiple of 8.  Entries at keys >= C are left untouched and may hold
+ * anything (they never reach an output of fpd_draft_block).               */
 int32_t fpd_fuse_context_kv(const fpd_drafter *d, const void *feats, int32_t B, int32_t C,
                             int32_t pos0, void *ctx_k, void *ctx_v, int32_t ctx_cap, void *ws,
                             size_t ws_bytes, void *stream);
