@@ -91,8 +91,8 @@ def cpu_baseline(wl, inp, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="traj2d3d")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bounded sample)")
@@ -185,6 +185,20 @@ def main():
         stream.synchronize()
     fuse_ms = f0.elapsed_time(f1) / reps
 
+    # incremental context: the last 8 positions re-appended at their offset,
+    # as a decode loop does after each committed block
+    n_app = min(8, C)
+    feats_tail = feats[:, :, C - n_app:].contiguous()
+    with torch.cuda.stream(stream):
+        fpd.fpd_append_context_kv(d, feats_tail, ck, cv, ws, pos0=C - n_app, stream=stream)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            fpd.fpd_append_context_kv(d, feats_tail, ck, cv, ws, pos0=C - n_app, stream=stream)
+        a1.record(stream)
+        stream.synchronize()
+    append_ms = a0.elapsed_time(a1) / reps
+
     # per-kernel durations: library-recorded HIP events over a second pass of the steps
     nprof = min(args.steps, 20)
     with torch.cuda.stream(stream):
@@ -248,6 +262,7 @@ def main():
                    "drafted_tokens_per_step": drafted},
         "latency_ms": {"p50": round(per_sorted[len(per) // 2], 4), "p90": round(per_sorted[int(len(per) * 0.9)], 4)},
         "fuse_context_ms": round(fuse_ms, 4),
+        f"append_context_{n_app}_ms": round(append_ms, 4),
         "cold_ms_per_step": round(fuse_ms + ms, 4),
         "roofline": roof,
         "kernels": kernels,

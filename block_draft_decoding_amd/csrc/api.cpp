@@ -349,12 +349,14 @@ int32_t fpd_workspace_size(const fpd_drafter* d, int32_t B, int32_t C, int32_t L
   return FPD_OK;
 }
 
-int32_t fpd_fuse_context_kv(const fpd_drafter* d, const void* feats, int32_t B, int32_t C, int32_t pos0,
-                            void* ctx_k, void* ctx_v, int32_t ctx_cap, void* ws, size_t ws_bytes,
-                            void* stream) {
-  if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
-  if (B < 1 || C < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C >= 1, pos0 >= 0");
-  if (ctx_cap < C || ctx_cap % 8) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
+}  // extern "C"
+
+namespace {
+
+// Fuses C positions of features and writes their K/V at key rows 0..C-1 of
+// the given layer-0 bases (strides from ctx_cap), keys rotated at rope_pos0 + c.
+int32_t fuse_rows(const fpd_drafter* d, const void* feats, int32_t B, int32_t C, int32_t rope_pos0, char* kbase,
+                  char* vbase, int32_t ctx_cap, void* ws, size_t ws_bytes, void* stream) {
   const FuseWs w = plan_fuse(*d, B, C);
   if (int32_t st = check_ws(ws, ws_bytes, w.total)) return st;
   const fpd_config& c = d->cfg;
@@ -374,14 +376,41 @@ int32_t fpd_fuse_context_kv(const fpd_drafter* d, const void* feats, int32_t B, 
   const size_t per_layer = (size_t)B * c.n_kv * ctx_cap * dh * d->esz;
   for (int li = 0; li < c.n_layers; ++li) {
     CtxOut o{};
-    o.k = (char*)ctx_k + li * per_layer;
-    o.vt = (char*)ctx_v + li * per_layer;
-    o.C = C, o.cap = ctx_cap, o.nkv = c.n_kv, o.d = dh, o.pos0 = pos0, o.rope = c.use_rope;
+    o.k = kbase + li * per_layer;
+    o.vt = vbase + li * per_layer;
+    o.C = C, o.cap = ctx_cap, o.nkv = c.n_kv, o.d = dh, o.pos0 = rope_pos0, o.rope = c.use_rope;
     o.tab = d->tab;
     const char* wkv = (const char*)d->layers[li].w_qkv + (size_t)c.n_q * dh * H * d->esz;
     FPD_TRY_HIP(gemm_ctx_kv(dt, Zn, M, H, wkv, o, part, w.partial_bytes, s));
   }
   return FPD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fpd_fuse_context_kv(const fpd_drafter* d, const void* feats, int32_t B, int32_t C, int32_t pos0,
+                            void* ctx_k, void* ctx_v, int32_t ctx_cap, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
+  if (B < 1 || C < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C >= 1, pos0 >= 0");
+  if (ctx_cap < C || ctx_cap % 8) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
+  return fuse_rows(d, feats, B, C, pos0, (char*)ctx_k, (char*)ctx_v, ctx_cap, ws, ws_bytes, stream);
+}
+
+int32_t fpd_append_context_kv(const fpd_drafter* d, const void* feats, int32_t B, int32_t C_new, int32_t pos0,
+                              void* ctx_k, void* ctx_v, int32_t ctx_cap, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
+  if (B < 1 || C_new < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C_new >= 1, pos0 >= 0");
+  if (ctx_cap % 8 || (int64_t)pos0 + C_new > ctx_cap)
+    return fail(FPD_E_SHAPE, "ctx_cap must be a multiple of 8 and hold pos0 + C_new keys");
+  // key row pos0 of every (layer, b, kv head) segment: the K rows are d
+  // elements long, the d-major V rows one element per key
+  const size_t esz = d->esz, dh = d->cfg.head_dim;
+  return fuse_rows(d, feats, B, C_new, pos0, (char*)ctx_k + (size_t)pos0 * dh * esz, (char*)ctx_v + (size_t)pos0 * esz,
+                   ctx_cap, ws, ws_bytes, stream);
 }
 
 int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L, const void* ctx_k,

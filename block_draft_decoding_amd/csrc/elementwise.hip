@@ -85,7 +85,7 @@ __device__ __forceinline__ void store_norm4<float>(float* dst, f32x4_t v, float 
 // and at most 4096 (the row stays in registers: 4 float4 per thread).
 // NS > 0: exactly NS split-K partials, all loads issued before the sums
 // (a runtime-length loop would serialise one memory round trip per split);
-// NS = 0: `splits` partials in a loop.
+// NS = 0: `splits` partials in batches of 8.
 template <class T, int NS>
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict__ partial, int splits, int M, int H,
                                                          float* __restrict__ h, const T* __restrict__ g, float eps,
@@ -118,9 +118,16 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
           acc = parts[0];
 #pragma unroll
           for (int s = 1; s < NS; ++s) acc += parts[s];
-        } else {
-          acc = pr[k];
-          for (int s = 1; s < splits; ++s) acc += pr[s * pstride + k];
+        } else {  // batches of 8 loads issued before their sums
+          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int s0 = 0; s0 < splits; s0 += 8) {
+            f32x4_t parts[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+              parts[s] = s0 + s < splits ? pr[(s0 + s) * pstride + k] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) acc += parts[s];
+          }
         }
         x += acc;
         hr[k] = x;

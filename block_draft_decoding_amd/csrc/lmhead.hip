@@ -238,31 +238,25 @@ __global__ __launch_bounds__(256) void head_f32_kernel(HeadArgs a) {
   }
 }
 
-// Best (value, column) of a row's chunk partials.  Loads go in batches of 8
-// issued before the comparisons, so a row costs one memory round trip per
-// 8 chunks rather than one per chunk.
+// Best (value, column) of a row's chunk partials, one wavefront per row:
+// lanes take every 64th chunk, then a butterfly leaves the row's best in
+// every lane (free text rows have ~1,200 chunks).
 __device__ __forceinline__ void best_of_row(const ReduceArgs& a, int row, int slot, float& v, int& c) {
+  const int lane = threadIdx.x & 63;
   v = -INFINITY;
   c = INT_MAX;
   const int nc = a.set_chunks[slot];
   const float* pv = a.pval + (size_t)row * a.max_chunks;
   const int32_t* pc = a.pcol + (size_t)row * a.max_chunks;
-  for (int k0 = 0; k0 < nc; k0 += 8) {
-    float v8[8];
-    int c8[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const bool ok = k0 + k < nc;
-      v8[k] = ok ? pv[k0 + k] : -INFINITY;
-      c8[k] = ok ? pc[k0 + k] : INT_MAX;
+  for (int k = lane; k < nc; k += 64) {
+    const float v2 = pv[k];
+    const int c2 = pc[k];
+    if (arg_better(v2, c2, v, c)) {
+      v = v2;
+      c = c2;
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (arg_better(v8[k], c8[k], v, c)) {
-        v = v8[k];
-        c = c8[k];
-      }
   }
+  wave_argmax(v, c, 64);
 }
 
 __device__ __forceinline__ int col_id(const ReduceArgs& a, int slot, int c) {
@@ -270,10 +264,12 @@ __device__ __forceinline__ int col_id(const ReduceArgs& a, int slot, int c) {
   return a.set_ids[slot] ? a.set_ids[slot][c] : c;
 }
 
-__global__ __launch_bounds__(256) void head_reduce_kernel(ReduceArgs a) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+// One wavefront per (request, position); lane 0 writes the decision.
+__global__ __launch_bounds__(64) void head_reduce_kernel(ReduceArgs a) {
+  const int idx = blockIdx.x;
   const int P = a.L - 1;
   if (idx >= a.B * P) return;
+  const bool lead = threadIdx.x == 0;
   const int b = idx / P, p = idx % P + 1;
   const int partner = a.partner[p];
   if (partner == -2) return;  // second position of a pair: decided with its first
@@ -292,6 +288,7 @@ __global__ __launch_bounds__(256) void head_reduce_kernel(ReduceArgs a) {
     best_of_row(a, qrow, qslot, vq, cq);
     const float on = v + vq;
     const float off = a.offv[idx] + a.offv[qrow];
+    if (!lead) return;
     if (off > on) {
       a.tokens[idx] = a.off_id;
       a.tokens[qrow] = a.off_id;
@@ -301,6 +298,7 @@ __global__ __launch_bounds__(256) void head_reduce_kernel(ReduceArgs a) {
     }
     return;
   }
+  if (!lead) return;
   int id = col_id(a, slot, c);
   if (offc >= 0) {
     const float vo = a.offv[idx];
@@ -343,7 +341,7 @@ hipError_t lm_head_reduce(const ReduceArgs& a, hipStream_t st) {
   ProfScope prof("lm_head_reduce", st);
   const int n = a.B * (a.L - 1);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(head_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(head_reduce_kernel, dim3(n), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

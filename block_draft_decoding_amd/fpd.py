@@ -86,6 +86,7 @@ _lay_destroy = _proto("fpd_layout_destroy", [vp])
 _lay_masks = _proto("fpd_layout_masks", [vp, ctypes.POINTER(fpd_layout_sizes), P_i32, P_i32, P_i32, P_i32, P_i32])
 _ws_size = _proto("fpd_workspace_size", [vp, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)])
 _fuse = _proto("fpd_fuse_context_kv", [vp, vp, i32, i32, i32, vp, vp, i32, vp, ctypes.c_size_t, vp])
+_append = _proto("fpd_append_context_kv", [vp, vp, i32, i32, i32, vp, vp, i32, vp, ctypes.c_size_t, vp])
 _draft = _proto("fpd_draft_block", [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_size_t, vp])
 _argmax = _proto("fpd_constrained_argmax", [vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, vp])
 _validate = _proto("fpd_validate_primitive", [vp, vp, i32, vp, vp, vp])
@@ -308,6 +309,16 @@ def fpd_fuse_context_kv(d: Drafter, feats: torch.Tensor, ctx_k: torch.Tensor, ct
     _check(_fuse(d.handle, _ptr(feats, "feats", d.dtype), B, C, pos0, _ptr(ctx_k, "ctx_k", d.dtype),
                  _ptr(ctx_v, "ctx_v", d.dtype), cap, _ptr(ws, "ws"), ws.numel(), _stream(stream)),
            "fpd_fuse_context_kv")
+
+
+def fpd_append_context_kv(d: Drafter, feats: torch.Tensor, ctx_k: torch.Tensor, ctx_v: torch.Tensor,
+                          ws: torch.Tensor, pos0: int, stream=None) -> None:
+    """feats [B, n_fused, C_new, H]: features of target positions pos0.. ."""
+    B, nt, C_new, H = feats.shape
+    cap = ctx_k.shape[3]
+    _check(_append(d.handle, _ptr(feats, "feats", d.dtype), B, C_new, pos0, _ptr(ctx_k, "ctx_k", d.dtype),
+                   _ptr(ctx_v, "ctx_v", d.dtype), cap, _ptr(ws, "ws"), ws.numel(), _stream(stream)),
+           "fpd_append_context_kv")
 
 
 def fpd_draft_block(d: Drafter, tokens: torch.Tensor, ctx_k: Optional[torch.Tensor],

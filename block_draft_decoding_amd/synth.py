@@ -109,6 +109,10 @@ def _bf16_ids(**over) -> Dict:
 
 DRAFTER_4B = DrafterShape(hidden=2560, n_q=32, n_kv=8, head_dim=128, n_layers=5,
                           inter=9728, vocab=151_936, n_fused=5, dtype="bf16")
+# FlashDrive's drafter: two layers, conditioned on the last 8 target tokens;
+# its widths are not printed, so the same 2560-wide layers are used.
+DRAFTER_2L = DrafterShape(hidden=2560, n_q=32, n_kv=8, head_dim=128, n_layers=2,
+                          inter=9728, vocab=151_936, n_fused=5, dtype="bf16")
 DRAFTER_TINY = DrafterShape(hidden=256, n_q=4, n_kv=2, head_dim=64, n_layers=2,
                             inter=704, vocab=2048, n_fused=2, dtype="f32")
 
@@ -141,6 +145,16 @@ WORKLOADS: Dict[str, Workload] = {
                          seed_index=4, off_row_std=0.06,
                          notes="Alpamayo-shaped 2D+3D trajectory, 64 waypoints x "
                                "(u, v, X, Y, Z, delim), L=385, paired off-frame rule"),
+    "flashdrive8": Workload("flashdrive8", DRAFTER_2L, batch=1, ctx=8,
+                            schema=dict(kind="text", block_len=8, **_bf16_ids()), seed_index=6,
+                            k_star=list(range(8)),
+                            notes="FlashDrive-shaped reasoning block: 2 layers, context = last 8 target "
+                                  "tokens, L=8, full vocabulary, prefix verification"),
+    "flashdrive16": Workload("flashdrive16", DRAFTER_2L, batch=1, ctx=8,
+                             schema=dict(kind="text", block_len=16, **_bf16_ids()), seed_index=7,
+                             k_star=list(range(16)),
+                             notes="FlashDrive-shaped reasoning block: 2 layers, context = last 8 target "
+                                   "tokens, L=16, full vocabulary, prefix verification"),
     "points3d": Workload("points3d", DRAFTER_4B, batch=8, ctx=4096,
                          schema=dict(kind="points3d_text", n_points=128, **_bf16_ids()),
                          seed_index=5,

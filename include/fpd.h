@@ -208,6 +208,21 @@ int32_t fpd_fuse_context_kv(const fpd_drafter *d, const void *feats, int32_t B, 
                             int32_t pos0, void *ctx_k, void *ctx_v, int32_t ctx_cap, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* Incremental context (VFlash paper §2.5: after a primitive or text block
+ * is committed, the target's forward pass updates the cache and the context
+ * features; FlashDrive §3.2, Fig. 4: the drafter is conditioned on the hidden
+ * states of the newest target tokens).  feats [B, n_fused, C_new, H] DT hold
+ * the selected layers' features of target positions pos0 .. pos0+C_new-1.
+ * They are fused exactly as in fpd_fuse_context_kv, and their K/V are written
+ * at key rows pos0 .. pos0+C_new-1 of ctx_k / ctx_v (same layouts), with keys
+ * rotated at those positions.  Other rows are untouched, so appending the
+ * context in pieces gives the caches of one fusion of the whole.  Needs
+ * pos0 + C_new <= ctx_cap (a multiple of 8).  Workspace as for
+ * fpd_fuse_context_kv with C = C_new.                                      */
+int32_t fpd_append_context_kv(const fpd_drafter *d, const void *feats, int32_t B, int32_t C_new,
+                              int32_t pos0, void *ctx_k, void *ctx_v, int32_t ctx_cap, void *ws,
+                              size_t ws_bytes, void *stream);
+
 /* One drafter forward over a block (VFlash paper §2.1-§2.2): tokens [B, L]
  * int32 = the anchor then the mask token at positions 1..L-1 (any ids in
  * [0, V) are accepted).  h = E[tokens]; then per layer (pre-norm, fp32

@@ -54,6 +54,9 @@ in the repository's design notes):
       and MLP inputs, final hidden), Q/K/V after RoPE, context K/V, the
       attention output and the SwiGLU product.  Everything else is carried
       at full precision (float64 here).  f32 workloads round nowhere.
+  R22 incremental context: features of newly committed target positions
+      pos0.. are fused exactly as the first context (R1, R2) and their K/V
+      written at cache rows pos0.. (cache row = target position).
 
 Functions whose result has no independent pin say so in their docstring.
 """
@@ -180,6 +183,28 @@ def fuse_context_kv(m: Model, feats: np.ndarray, ctx_pos0: int = 0):
         ks.append(_store(m._rope(k, pos), m.dtype))
         vs.append(_store(v, m.dtype))
     return np.stack(ks), np.stack(vs)
+
+
+def append_context_kv(m: Model, ctx_k: np.ndarray, ctx_v: np.ndarray, feats: np.ndarray, pos0: int):
+    """Incremental context: after a block is accepted the target's forward
+    pass updates its cache and the context features (VFlash paper §2.5), and
+    the drafter is conditioned on the newest target positions (FlashDrive
+    §3.2, Fig. 4: the hidden states of the last eight target tokens).  feats [B, n_t, C_new, H] are the
+    fused-layer features of target positions pos0 .. pos0 + C_new - 1; their
+    K/V (keys rotated at those positions) replace rows pos0 .. of the given
+    caches [n_layers, B, C, n_kv, d], which grow if needed (R22).  Rows
+    before pos0 are returned unchanged."""
+    nk, nv = fuse_context_kv(m, feats, ctx_pos0=pos0)
+    Cn = nk.shape[2]
+    N, B, C0 = ctx_k.shape[0], ctx_k.shape[1], ctx_k.shape[2]
+    C = max(C0, pos0 + Cn)
+    out_k = np.zeros((N, B, C) + ctx_k.shape[3:], np.float64)
+    out_v = np.zeros((N, B, C) + ctx_v.shape[3:], np.float64)
+    out_k[:, :, :C0] = ctx_k
+    out_v[:, :, :C0] = ctx_v
+    out_k[:, :, pos0:pos0 + Cn] = nk
+    out_v[:, :, pos0:pos0 + Cn] = nv
+    return out_k, out_v
 
 
 # ---------------------------------------------------------------------------

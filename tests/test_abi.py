@@ -140,6 +140,13 @@ def test_hot_calls_reject_bad_arguments_without_gpu_work():
         assert fpd._draft(h, 8, 1, 16, 8, 8, 64, 32, 64, 8, None, 0, None) == fpd.FPD_E_SHAPE
         # capacity not a multiple of 8
         assert fpd._fuse(h, 8, 1, 60, 0, 8, 8, 62, None, 0, None) == fpd.FPD_E_SHAPE
+        # appended rows past the capacity, negative offset, no rows, null features
+        assert fpd._append(h, 8, 1, 8, 60, 8, 8, 64, None, 0, None) == fpd.FPD_E_SHAPE
+        assert fpd._append(h, 8, 1, 8, -1, 8, 8, 64, None, 0, None) == fpd.FPD_E_SHAPE
+        assert fpd._append(h, 8, 1, 0, 0, 8, 8, 64, None, 0, None) == fpd.FPD_E_SHAPE
+        assert fpd._append(h, None, 1, 8, 0, 8, 8, 64, None, 0, None) == fpd.FPD_E_ARG
+        # in range but the workspace is missing
+        assert fpd._append(h, 8, 1, 8, 56, 8, 8, 64, 8, 16, None) == fpd.FPD_E_WORKSPACE
         # workspace too small
         assert fpd._draft(h, 8, 1, 16, 8, 8, 64, 64, 64, 8, 8, 16, None) == fpd.FPD_E_WORKSPACE
         assert fpd._argmax(h, None, 8, 1, 8, None, 8, 1 << 20, None) == fpd.FPD_E_ARG

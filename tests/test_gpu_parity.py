@@ -222,7 +222,7 @@ def test_determinism_bitwise():
 
 # ---- full-size workloads ------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["text", "traj2d", "traj2d3d"])
+@pytest.mark.parametrize("name", ["text", "traj2d", "traj2d3d", "flashdrive8", "flashdrive16"])
 def test_full_size_workload(name):
     wl, inp = workload_inputs(name)
     g = GpuCase(wl, inp)
@@ -234,15 +234,15 @@ def test_full_size_workload(name):
     res = oracle_result(name)
     compare_all(wl, g, lg, res, "bf16", f"full {name}")
     lay = res["layout"]
-    if name == "text":
-        B = wl.batch
-        draft = np.repeat(res["tokens"], 16, axis=0)
-        tgt = synth.plant_targets(draft, np.arange(16), wl.shape.vocab, 3002)
-        kk = torch.empty(16, dtype=torch.int32, device="cuda")
+    if wl.schema["kind"] == "text":
+        n = lay.L                  # every accepted length 0 .. L-1
+        draft = np.repeat(res["tokens"], n, axis=0)
+        tgt = synth.plant_targets(draft, np.arange(n), wl.shape.vocab, 3000 + wl.seed_index)
+        kk = torch.empty(n, dtype=torch.int32, device="cuda")
         nx = torch.empty_like(kk)
         g.fpd.fpd_verify_prefix(torch.from_numpy(draft).cuda(), torch.from_numpy(tgt).cuda(), kk, nx)
-        assert np.array_equal(kk.cpu().numpy(), np.arange(16))
-        assert np.array_equal(nx.cpu().numpy(), tgt[np.arange(16), np.arange(16)])
+        assert np.array_equal(kk.cpu().numpy(), np.arange(n))
+        assert np.array_equal(nx.cpu().numpy(), tgt[np.arange(n), np.arange(n)])
     else:
         k, f = g.validate()
         ko, fo = O.validate_primitive(g.toks.cpu().numpy(), lay)
@@ -355,3 +355,28 @@ def test_validator_large_sets_from_global_memory():
     ko, fo = O.validate_primitive(toks, lay)
     assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
     assert 0 < int((ko == 0).sum()) < B
+
+
+def test_append_context_in_pieces_matches_one_fusion():
+    """Incremental context: the context appended in three pieces at their
+    own positions (the decode loop after each committed block) gives the
+    oracle's caches of one fusion of the whole context, and the same block
+    output; keys before each piece are untouched by it."""
+    from block_draft_decoding_amd import fpd
+    wl = small_workload("traj2d3d", 2, 40, seed=66, n_points=3, off_id=4099 - 1020 + 1002)
+    inp = synth.make_inputs(wl)
+    g = GpuCase(wl, inp)
+    cap = 48
+    g.cap = cap
+    g.ws = fpd.alloc_workspace(g.d, g.B, cap, g.L)
+    g.ctx_k, g.ctx_v = fpd.alloc_context(g.d, g.B, cap)
+    for a, b in ((0, 7), (7, 16), (16, 40)):
+        before_k = g.ctx_k[:, :, :, :a].clone()
+        fpd.fpd_append_context_kv(g.d, g.feats[:, :, a:b].contiguous(), g.ctx_k, g.ctx_v, g.ws, pos0=a)
+        torch.cuda.synchronize()
+        assert torch.equal(g.ctx_k[:, :, :, :a], before_k)
+    g.draft()
+    lg = g.argmax(logits=True)
+    torch.cuda.synchronize()
+    res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
+    compare_all(wl, g, lg, res, "bf16", "appended context")

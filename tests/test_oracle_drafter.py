@@ -157,3 +157,45 @@ def test_bf16_storage_points():
     hid2 = O.draft_block(m_nr, tokens, ck2, cv2)
     rel = np.abs(hid - hid2).max() / np.abs(hid2).max()
     assert 1e-5 < rel < 3e-2
+
+
+def test_append_in_chunks_equals_one_fusion():
+    """Appending the context in pieces (each piece's keys rotated at its own
+    positions) gives the caches of fusing the whole context at once, and the
+    drafter output over them is the same; rows before pos0 are untouched."""
+    s, m = _model(seed=21)
+    rng = np.random.default_rng(4)
+    B, C = 2, 13
+    feats = rng.standard_normal((B, s.n_fused, C, s.hidden))
+    k_all, v_all = O.fuse_context_kv(m, feats)
+    ck = np.zeros((s.n_layers, B, 0, s.n_kv, s.head_dim))
+    cv = np.zeros_like(ck)
+    for a, b in ((0, 4), (4, 5), (5, 13)):
+        before = ck.copy()
+        ck, cv = O.append_context_kv(m, ck, cv, feats[:, :, a:b], pos0=a)
+        assert np.array_equal(ck[:, :, :a], before[:, :, :a])
+    np.testing.assert_allclose(ck, k_all, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(cv, v_all, rtol=1e-12, atol=1e-12)
+    tokens = rng.integers(0, s.vocab, size=(B, 6)).astype(np.int32)
+    h1 = O.draft_block(m, tokens, ck, cv)
+    h2 = O.draft_block(m, tokens, k_all, v_all)
+    np.testing.assert_allclose(h1, h2, rtol=1e-11, atol=1e-11)
+
+
+def test_append_overwrites_only_its_rows():
+    """A re-appended position (a target re-decode of the same slot) replaces
+    exactly its own rows, with keys rotated at that slot's position."""
+    s, m = _model(seed=22)
+    rng = np.random.default_rng(5)
+    B, C = 1, 9
+    feats = rng.standard_normal((B, s.n_fused, C, s.hidden))
+    ck, cv = O.fuse_context_kv(m, feats)
+    newf = rng.standard_normal((B, s.n_fused, 2, s.hidden))
+    k2, v2 = O.append_context_kv(m, ck, cv, newf, pos0=3)
+    ref_k, ref_v = O.fuse_context_kv(m, newf, ctx_pos0=3)
+    assert np.array_equal(k2[:, :, :3], ck[:, :, :3]) and np.array_equal(k2[:, :, 5:], ck[:, :, 5:])
+    np.testing.assert_allclose(k2[:, :, 3:5], ref_k, rtol=0, atol=0)
+    np.testing.assert_allclose(v2[:, :, 3:5], ref_v, rtol=0, atol=0)
+    # the same features fused at position 0 differ (keys are position-dependent)
+    k0, _ = O.fuse_context_kv(m, newf, ctx_pos0=0)
+    assert not np.allclose(k0, ref_k)
