@@ -73,7 +73,7 @@ def cpu_baseline(wl, inp, budget_s):
     t_all = time.time()
     while len(times) < 3 and (not times or time.time() - t_all + times[-1] < budget_s):
         t = time.time()
-        hid = O.draft_block(m, inp.tokens, ck, cv)
+        hid = (O.draft_blocks_shared if wl.shared_ctx else O.draft_block)(m, inp.tokens, ck, cv)
         z = O.full_logits(m, hid)
         toks = O.constrained_tokens(z, lay)
         if wl.schema["kind"] == "text":
@@ -130,7 +130,9 @@ def main():
     L, B, C = lay.L, wl.batch, wl.ctx
     cap = (C + 7) // 8 * 8
     ws = fpd.alloc_workspace(d, B, cap, L)
-    ck, cv = fpd.alloc_context(d, B, cap)
+    shared = wl.shared_ctx          # several blocks against one observation
+    ck, cv = fpd.alloc_context(d, 1 if shared else B, cap)
+    draft = fpd.fpd_draft_blocks_shared_ctx if shared else fpd.fpd_draft_block
     feats = fpd.to_device(inp.feats, dt)
     tokens = torch.from_numpy(inp.tokens).cuda()
     hidden = torch.empty(B, L - 1, s.hidden, dtype=dt, device="cuda")
@@ -143,7 +145,7 @@ def main():
 
     with torch.cuda.stream(stream):
         fpd.fpd_fuse_context_kv(d, feats, ck, cv, ws, stream=stream)
-        fpd.fpd_draft_block(d, tokens, ck, cv, C, hidden, ws, stream=stream)
+        draft(d, tokens, ck, cv, C, hidden, ws, stream=stream)
         fpd.fpd_constrained_argmax(d, lay, hidden, toks, ws, stream=stream)
     stream.synchronize()
     target = None
@@ -151,7 +153,7 @@ def main():
         target = torch.from_numpy(synth.plant_targets(toks.cpu().numpy(), 7, s.vocab, 3000 + wl.seed_index)).cuda()
 
     def step():
-        fpd.fpd_draft_block(d, tokens, ck, cv, C, hidden, ws, stream=stream)
+        draft(d, tokens, ck, cv, C, hidden, ws, stream=stream)
         fpd.fpd_constrained_argmax(d, lay, hidden, toks, ws, stream=stream)
         if text:
             fpd.fpd_verify_prefix(toks, target, k_out, aux, stream=stream)

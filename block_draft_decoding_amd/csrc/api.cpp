@@ -413,9 +413,13 @@ int32_t fpd_append_context_kv(const fpd_drafter* d, const void* feats, int32_t B
                    ctx_cap, ws, ws_bytes, stream);
 }
 
-int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L, const void* ctx_k,
-                        const void* ctx_v, int32_t C, int32_t ctx_cap, int32_t block_pos, void* hidden_out,
-                        void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L, const void* ctx_k,
+                   const void* ctx_v, int32_t C, int32_t ctx_cap, int32_t block_pos, void* hidden_out, void* ws,
+                   size_t ws_bytes, void* stream, bool shared_ctx) {
   if (!d || !tokens || !hidden_out) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || L < 2 || C < 0 || block_pos < 0) return fail(FPD_E_SHAPE, "need B >= 1, L >= 2, C >= 0, block_pos >= 0");
   if (C > 0 && (!ctx_k || !ctx_v)) return fail(FPD_E_ARG, "null context");
@@ -430,7 +434,7 @@ int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, 
   float* part = (float*)wsp(ws, w.partial);
   // h = E[tokens], a = RMSNorm(h) (the first layer's attention norm)
   FPD_TRY_HIP(embed_norm(dt, tokens, M, d->w.embed, H, c.vocab, h, d->layers[0].g_attn, c.rms_eps, a, s));
-  const size_t ctx_layer = (size_t)B * c.n_kv * (size_t)ctx_cap * dh * d->esz;
+  const size_t ctx_layer = (size_t)(shared_ctx ? 1 : B) * c.n_kv * (size_t)ctx_cap * dh * d->esz;
   for (int li = 0; li < c.n_layers; ++li) {
     const fpd_layer_weights& lw = d->layers[li];
     QkvOut qo{};
@@ -444,6 +448,7 @@ int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, 
     at.cvt = C > 0 ? (const char*)ctx_v + li * ctx_layer : nullptr;
     at.o = wsp(ws, w.o);
     at.B = B, at.L = L, at.Lp = qo.Lp, at.C = C, at.cap = ctx_cap, at.nq = c.n_q, at.nkv = c.n_kv, at.d = dh;
+    at.ctx_bstride = shared_ctx ? 0 : 1;
     at.scale = (float)(1.0 / std::sqrt((double)dh));
     FPD_TRY_HIP(attention(dt, at, wsp(ws, w.attn), w.attn_bytes, s));
     // h += O W_o^T, a = RMSNorm(h) for the MLP
@@ -458,6 +463,22 @@ int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, 
                                    "gemm_down"));
   }
   return FPD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L, const void* ctx_k,
+                        const void* ctx_v, int32_t C, int32_t ctx_cap, int32_t block_pos, void* hidden_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return draft_impl(d, tokens, B, L, ctx_k, ctx_v, C, ctx_cap, block_pos, hidden_out, ws, ws_bytes, stream, false);
+}
+
+int32_t fpd_draft_blocks_shared_ctx(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L,
+                                    const void* ctx_k, const void* ctx_v, int32_t C, int32_t ctx_cap,
+                                    int32_t block_pos, void* hidden_out, void* ws, size_t ws_bytes, void* stream) {
+  return draft_impl(d, tokens, B, L, ctx_k, ctx_v, C, ctx_cap, block_pos, hidden_out, ws, ws_bytes, stream, true);
 }
 
 int32_t fpd_constrained_argmax(const fpd_drafter* d, const fpd_layout* lay, const void* hidden, int32_t B,

@@ -40,7 +40,7 @@ struct AttnP {
   bf16_t* o;
   float* opart;   // [splits, B, nq, L, D]
   float* mlpart;  // [splits, B, nq, L, 2]
-  int B, L, Lp, C, cap, nq, nkv, g, R, q_tiles, splits, ctx_tiles, blk_tiles;
+  int B, L, Lp, C, cap, nq, nkv, g, R, q_tiles, splits, ctx_tiles, blk_tiles, ctx_bstride;
   float scale_log2;
 };
 
@@ -85,13 +85,14 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
   const int total = p.ctx_tiles + p.blk_tiles;
   const int t0 = (int)((long)sp * total / p.splits), t1 = (int)((long)(sp + 1) * total / p.splits);
   const size_t bhk = (size_t)b * p.nkv + j;
+  const size_t cbhk = (size_t)b * p.ctx_bstride * p.nkv + j;  // context segment (shared: b = 0)
 
   const __amdgpu_buffer_rsrc_t kc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.ck + bhk * p.cap * D), (short)0, (int)((size_t)p.cap * D * 2), 0x00020000);
+      (void*)(p.ck + cbhk * p.cap * D), (short)0, (int)((size_t)p.cap * D * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t kbk = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.kb + bhk * p.L * D), (short)0, (int)((size_t)p.L * D * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.cvt + bhk * D * p.cap), (short)0, (int)((size_t)D * p.cap * 2), 0x00020000);
+      (void*)(p.cvt + cbhk * D * p.cap), (short)0, (int)((size_t)D * p.cap * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vbk = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.vbt + bhk * D * p.Lp), (short)0, (int)((size_t)D * p.Lp * 2), 0x00020000);
   // per-lane source offsets of the slots this lane fills (the swizzle is
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ vbt, const float* __restrict__ ck,
                                                       const float* __restrict__ cvt, float* __restrict__ o,
                                                       int B, int L, int Lp, int C, int cap, int nq, int nkv,
-                                                      float scale) {
+                                                      int ctx_bstride, float scale) {
   __shared__ float red_o[64][DD + 1];
   __shared__ float red_m[64], red_l[64];
   const int lane = threadIdx.x;
@@ -315,6 +316,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   const int l = row % L, bh = row / L, head = bh % nq, b = bh / nq;
   const int j = (head * nkv) / nq;
   const size_t bhk = (size_t)b * nkv + j;
+  const size_t cbhk = (size_t)b * ctx_bstride * nkv + j;  // context segment (shared: b = 0)
   float qv[DD];
   const float* qp = q + (((size_t)b * nq + head) * L + l) * DD;
 #pragma unroll
@@ -329,8 +331,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
     const float* vp;
     int ldv;
     if (key < C) {
-      kp = ck + (bhk * cap + key) * DD;
-      vp = cvt + bhk * DD * cap + key;
+      kp = ck + (cbhk * cap + key) * DD;
+      vp = cvt + cbhk * DD * cap + key;
       ldv = cap;
     } else {
       kp = kb + (bhk * L + (key - C)) * DD;
@@ -401,6 +403,7 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     p.cvt = (const bf16_t*)a.cvt;
     p.o = (bf16_t*)a.o;
     p.B = a.B, p.L = a.L, p.Lp = a.Lp, p.C = a.C, p.cap = a.cap, p.nq = a.nq, p.nkv = a.nkv;
+    p.ctx_bstride = a.ctx_bstride;
     p.g = a.nq / a.nkv;
     p.R = p.g * a.L;
     int total = 0;
@@ -443,11 +446,11 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
   if (a.d == 64)
     hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(rows), dim3(64), 0, st, (const float*)a.q,
                        (const float*)a.kb, (const float*)a.vbt, (const float*)a.ck, (const float*)a.cvt,
-                       (float*)a.o, a.B, a.L, a.Lp, a.C, a.cap, a.nq, a.nkv, a.scale);
+                       (float*)a.o, a.B, a.L, a.Lp, a.C, a.cap, a.nq, a.nkv, a.ctx_bstride, a.scale);
   else
     hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(rows), dim3(64), 0, st, (const float*)a.q,
                        (const float*)a.kb, (const float*)a.vbt, (const float*)a.ck, (const float*)a.cvt,
-                       (float*)a.o, a.B, a.L, a.Lp, a.C, a.cap, a.nq, a.nkv, a.scale);
+                       (float*)a.o, a.B, a.L, a.Lp, a.C, a.cap, a.nq, a.nkv, a.ctx_bstride, a.scale);
   return hipGetLastError();
 }
 

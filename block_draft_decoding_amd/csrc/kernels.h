@@ -123,6 +123,7 @@ struct AttnArgs {
   const void* cvt;    // [B, nkv, d, cap]
   void* o;            // [B, L, nq * d]
   int B, L, Lp, C, cap, nq, nkv, d;
+  int ctx_bstride;    // 1: request b reads context b; 0: every request reads context 0 (shared)
   float scale;
 };
 size_t attention_scratch_bytes(int dt, int B, int L, int C, int nq, int nkv, int d);

@@ -83,6 +83,7 @@ class Workload:
     off_row_std: Optional[float] = None   # std of the OFF row of the LM head, if drawn apart
     k_star: Optional[List[int]] = None    # planted accepted lengths for text verification
     notes: str = ""
+    shared_ctx: bool = False              # all blocks share one context (features of batch 1)
 
     @property
     def block_len(self) -> int:
@@ -155,6 +156,11 @@ WORKLOADS: Dict[str, Workload] = {
                              k_star=list(range(16)),
                              notes="FlashDrive-shaped reasoning block: 2 layers, context = last 8 target "
                                    "tokens, L=16, full vocabulary, prefix verification"),
+    "traj2d_shared16": Workload("traj2d_shared16", DRAFTER_4B, batch=16, ctx=2048,
+                                schema=dict(kind="traj2d", n_points=8, **_bf16_ids()), seed_index=8,
+                                shared_ctx=True,
+                                notes="16 NAVSIM-shaped 2D-trajectory blocks (L=25) against one shared "
+                                      "context of 2048 positions: M = 400 projection rows"),
     "points3d": Workload("points3d", DRAFTER_4B, batch=8, ctx=4096,
                          schema=dict(kind="points3d_text", n_points=128, **_bf16_ids()),
                          seed_index=5,
@@ -280,10 +286,13 @@ def make_features(shape: DrafterShape, batch: int, ctx: int, seed: int) -> np.nd
     return _store(f, shape.dtype)
 
 
-def make_block_tokens(shape: DrafterShape, schema: Dict, batch: int, seed: int) -> np.ndarray:
+def make_block_tokens(shape: DrafterShape, schema: Dict, batch: int, seed: int,
+                      distinct_anchors: bool = False) -> np.ndarray:
     """Block input tokens [B, L]: anchor then MASK at every other position.
     Primitive blocks start with the typed start token; text blocks (and the
-    tiny drafter) start with a drawn anchor."""
+    tiny drafter) start with a drawn anchor.  distinct_anchors: blocks after
+    the first draw their anchor (several primitives from one observation
+    differ by their start token)."""
     L = schema_block_len(schema)
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=seed, spawn_key=(1,))))
     tok = np.full((batch, L), schema["mask_id"], np.int32)
@@ -293,6 +302,8 @@ def make_block_tokens(shape: DrafterShape, schema: Dict, batch: int, seed: int) 
         tok[:, 0] = rng.integers(0, 1000, size=batch)
     else:
         tok[:, 0] = schema["start_id"]
+    if distinct_anchors and batch > 1:
+        tok[1:, 0] = rng.integers(0, shape.vocab - 1, size=batch - 1)
     return tok
 
 
@@ -331,8 +342,8 @@ def make_inputs(wl: Workload, weights: Optional[Weights] = None, zero: tuple = (
         weights = make_weights(wl.shape, 1000 + k,
                                off_row=off_row if (off_row is not None and off_row >= 0) else None,
                                off_row_std=wl.off_row_std, zero=zero)
-    feats = make_features(wl.shape, wl.batch, wl.ctx, 2000 + k)
-    tokens = make_block_tokens(wl.shape, wl.schema, wl.batch, 3000 + k)
+    feats = make_features(wl.shape, 1 if wl.shared_ctx else wl.batch, wl.ctx, 2000 + k)
+    tokens = make_block_tokens(wl.shape, wl.schema, wl.batch, 3000 + k, distinct_anchors=wl.shared_ctx)
     return Inputs(wl, weights, feats, tokens)
 
 

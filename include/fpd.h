@@ -239,6 +239,19 @@ int32_t fpd_draft_block(const fpd_drafter *d, const int32_t *tokens, int32_t B, 
                         int32_t block_pos, void *hidden_out, void *ws, size_t ws_bytes,
                         void *stream);
 
+/* Several primitives against one shared observation (VFlash paper,
+ * conclusion and future work: complementary primitives predicted from one
+ * observation).  Same as fpd_draft_block for B blocks of the same length L,
+ * except that every block attends to the one context in ctx_k
+ * [n_layers, 1, n_kv, ctx_cap, d] / ctx_v [n_layers, 1, n_kv, d, ctx_cap]
+ * (written by fpd_fuse_context_kv / fpd_append_context_kv with B = 1).
+ * The projections then run on M = B*L rows at the weight bytes of one block.
+ * tokens [B, L]: each block's own anchor, then mask tokens.                */
+int32_t fpd_draft_blocks_shared_ctx(const fpd_drafter *d, const int32_t *tokens, int32_t B, int32_t L,
+                                    const void *ctx_k, const void *ctx_v, int32_t C, int32_t ctx_cap,
+                                    int32_t block_pos, void *hidden_out, void *ws, size_t ws_bytes,
+                                    void *stream);
+
 /* Constrained decoding (VFlash paper §2.5).  hidden [B, L-1, H] DT from
  * fpd_draft_block.  For each position p the logits z_p[s] = h_p . W_lm[s]
  * are computed only for s in the legal set S_p (every id for free

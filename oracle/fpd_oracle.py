@@ -56,7 +56,10 @@ in the repository's design notes):
       at full precision (float64 here).  f32 workloads round nowhere.
   R22 incremental context: features of newly committed target positions
       pos0.. are fused exactly as the first context (R1, R2) and their K/V
-      written at cache rows pos0.. (cache row = target position).
+      written at cache rows pos0.. (cache row = target position);
+  R23 several primitives from one observation: blocks of one length, each
+      with its own anchor, attend to one shared context and to their own
+      block only (no attention between blocks).
 
 Functions whose result has no independent pin say so in their docstring.
 """
@@ -272,6 +275,18 @@ def draft_block(m: Model, tokens: np.ndarray, ctx_k: np.ndarray, ctx_v: np.ndarr
     if return_residuals:
         return out, np.stack(resid, axis=1)
     return out
+
+
+def draft_blocks_shared(m: Model, tokens: np.ndarray, ctx_k: np.ndarray, ctx_v: np.ndarray,
+                        block_pos: Optional[int] = None) -> np.ndarray:
+    """Several blocks against one shared observation (VFlash paper,
+    conclusion / future work: complementary primitives from one
+    observation): every block of tokens [B, L] attends to the single
+    context ctx_k / ctx_v [n_layers, 1, C, n_kv, d] (R23).  Returns [B, L-1, H]."""
+    B = np.asarray(tokens).shape[0]
+    bk = np.broadcast_to(ctx_k, ctx_k.shape[:1] + (B,) + ctx_k.shape[2:])
+    bv = np.broadcast_to(ctx_v, ctx_v.shape[:1] + (B,) + ctx_v.shape[2:])
+    return draft_block(m, tokens, bk, bv, block_pos=block_pos)
 
 
 def full_logits(m: Model, hidden: np.ndarray, chunk_rows: int = 8192) -> np.ndarray:
@@ -528,14 +543,19 @@ def verify_prefix(draft: np.ndarray, target: np.ndarray):
 # ---------------------------------------------------------------------------
 
 def run_block(m: Model, feats, tokens, schema: Dict, targets=None, ctx_pos0: int = 0,
-              block_pos: Optional[int] = None, want_logits: bool = False):
+              block_pos: Optional[int] = None, want_logits: bool = False, shared_ctx: bool = False):
     """Fuse, draft, decode under the layout, then accept.  Returns a dict
     with ctx_k, ctx_v, hidden, tokens, (logits), k_prim/first_invalid for
-    primitive layouts and k_text/next when target tokens are given."""
+    primitive layouts and k_text/next when target tokens are given.
+    shared_ctx: feats hold one context that every block attends to (R23)."""
     lay = build_layout(schema, m.V)
     ck, cv = fuse_context_kv(m, feats, ctx_pos0)
     C = ck.shape[2]
-    hidden = draft_block(m, tokens, ck, cv, block_pos=(C + ctx_pos0) if block_pos is None else block_pos)
+    bp = (C + ctx_pos0) if block_pos is None else block_pos
+    if shared_ctx:
+        hidden = draft_blocks_shared(m, tokens, ck, cv, block_pos=bp)
+    else:
+        hidden = draft_block(m, tokens, ck, cv, block_pos=bp)
     z = full_logits(m, hidden)
     toks = constrained_tokens(z, lay)
     res = dict(ctx_k=ck, ctx_v=cv, hidden=hidden, tokens=toks, layout=lay)

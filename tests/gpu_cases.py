@@ -159,9 +159,10 @@ class GpuCase:
         self.d = fpd.fpd_drafter_create(fpd.make_config(shape), self.w)
         self.lay = fpd.fpd_layout_create(self.d, wl.schema)
         self.B, self.C, self.L = wl.batch, wl.ctx, self.lay.L
+        self.shared = wl.shared_ctx
         self.cap = round8(max(self.C, 8))
         self.ws = fpd.alloc_workspace(self.d, self.B, self.cap, self.L)
-        self.ctx_k, self.ctx_v = fpd.alloc_context(self.d, self.B, self.cap)
+        self.ctx_k, self.ctx_v = fpd.alloc_context(self.d, 1 if self.shared else self.B, self.cap)
         self.feats = fpd.to_device(inp.feats, self.dt) if self.C > 0 else None
         self.tokens = torch.from_numpy(inp.tokens).cuda()
         H = shape.hidden
@@ -174,6 +175,10 @@ class GpuCase:
             self.fpd.fpd_fuse_context_kv(self.d, self.feats, self.ctx_k, self.ctx_v, self.ws, pos0=pos0)
 
     def draft(self, block_pos=None):
+        if self.shared:
+            self.fpd.fpd_draft_blocks_shared_ctx(self.d, self.tokens, self.ctx_k, self.ctx_v, self.C, self.hidden,
+                                                 self.ws, block_pos=block_pos)
+            return
         self.fpd.fpd_draft_block(self.d, self.tokens, self.ctx_k if self.C else None,
                                  self.ctx_v if self.C else None, self.C, self.hidden, self.ws, block_pos=block_pos)
 
@@ -210,6 +215,6 @@ def oracle_result(name: str):
     wl, inp = workload_inputs(name)
     t = time.time()
     m = O.Model(wl.shape, inp.weights)
-    res = O.run_block(m, inp.feats, inp.tokens, wl.schema, want_logits=True)
+    res = O.run_block(m, inp.feats, inp.tokens, wl.schema, want_logits=True, shared_ctx=wl.shared_ctx)
     progress(f"[oracle] {name} done in {time.time() - t:.1f}s")
     return res

@@ -21,12 +21,12 @@ SMALL = synth.DrafterShape(hidden=512, n_q=8, n_kv=2, head_dim=128, n_layers=2, 
                            n_fused=3, dtype="bf16", weight_std=0.02)
 
 
-def small_workload(kind, B, C, seed, shape=SMALL, **schema_over):
+def small_workload(kind, B, C, seed, shape=SMALL, shared_ctx=False, **schema_over):
     ids = small_ids(shape.vocab)
     schema = dict(kind=kind, **ids)
     schema.update(schema_over)
     return synth.Workload(f"small-{kind}", shape, batch=B, ctx=C, schema=schema, seed_index=seed,
-                          off_row_std=0.06 if schema.get("off_id", -1) >= 0 else None)
+                          off_row_std=0.06 if schema.get("off_id", -1) >= 0 else None, shared_ctx=shared_ctx)
 
 
 def run_both(wl, n_layers=None, logits=True):
@@ -38,7 +38,8 @@ def run_both(wl, n_layers=None, logits=True):
     torch.cuda.synchronize()
     shape = wl.shape if n_layers is None else replace(wl.shape, n_layers=n_layers)
     w = inp.weights if n_layers is None else replace(inp.weights, layers=inp.weights.layers[:n_layers])
-    res = O.run_block(O.Model(shape, w), inp.feats, inp.tokens, wl.schema, want_logits=True)
+    res = O.run_block(O.Model(shape, w), inp.feats, inp.tokens, wl.schema, want_logits=True,
+                      shared_ctx=wl.shared_ctx)
     return inp, g, lg, res
 
 
@@ -222,7 +223,8 @@ def test_determinism_bitwise():
 
 # ---- full-size workloads ------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["text", "traj2d", "traj2d3d", "flashdrive8", "flashdrive16"])
+@pytest.mark.parametrize("name", ["text", "traj2d", "traj2d3d", "flashdrive8", "flashdrive16",
+                                  "traj2d_shared16"])
 def test_full_size_workload(name):
     wl, inp = workload_inputs(name)
     g = GpuCase(wl, inp)
@@ -380,3 +382,14 @@ def test_append_context_in_pieces_matches_one_fusion():
     torch.cuda.synchronize()
     res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
     compare_all(wl, g, lg, res, "bf16", "appended context")
+
+
+def test_blocks_share_one_context():
+    """Several primitives against one observation: three blocks with their
+    own anchors attend to one shared context (no copy per block)."""
+    wl = small_workload("traj2d3d", 3, 77, seed=67, shared_ctx=True, n_points=5, off_id=4099 - 1020 + 1002)
+    inp, g, lg, res = run_both(wl)
+    assert g.ctx_k.shape[1] == 1
+    compare_all(wl, g, lg, res, "bf16", "shared context")
+    toks = res["tokens"]
+    assert not np.array_equal(toks[0], toks[1])   # distinct anchors give distinct blocks

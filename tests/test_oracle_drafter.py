@@ -199,3 +199,21 @@ def test_append_overwrites_only_its_rows():
     # the same features fused at position 0 differ (keys are position-dependent)
     k0, _ = O.fuse_context_kv(m, newf, ctx_pos0=0)
     assert not np.allclose(k0, ref_k)
+
+
+def test_shared_context_equals_separate_runs():
+    """Blocks against one shared context give each block's own single-block
+    run over that context (no attention crosses blocks), with the context
+    broadcast rather than copied."""
+    s, m = _model(seed=23)
+    rng = np.random.default_rng(6)
+    C, B, L = 11, 3, 7
+    feats = rng.standard_normal((1, s.n_fused, C, s.hidden))
+    ck, cv = O.fuse_context_kv(m, feats)
+    tokens = rng.integers(0, s.vocab, size=(B, L)).astype(np.int32)
+    h = O.draft_blocks_shared(m, tokens, ck, cv)
+    for b in range(B):
+        hb = O.draft_block(m, tokens[b:b + 1], ck, cv)
+        np.testing.assert_array_equal(h[b], hb[0])
+    # blocks differing only in their anchor still differ: the anchor matters
+    assert not np.allclose(h[0], h[1])
