@@ -201,6 +201,20 @@ def main():
         stream.synchronize()
     append_ms = a0.elapsed_time(a1) / reps
 
+    # coordinate codec on the drafted block: tokens -> bin values, as a caller
+    # reads the trajectory out of each block
+    vals = torch.empty(toks.numel(), dtype=torch.float64, device="cuda")
+    cb = wl.schema.get("coord_base", 0)
+    with torch.cuda.stream(stream):
+        fpd.fpd_tokens_to_coords(toks, vals, cb, stream=stream)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(reps):
+            fpd.fpd_tokens_to_coords(toks, vals, cb, stream=stream)
+        c1.record(stream)
+        stream.synchronize()
+    decode_ms = c0.elapsed_time(c1) / reps
+
     # per-kernel durations: library-recorded HIP events over a second pass of the steps
     nprof = min(args.steps, 20)
     with torch.cuda.stream(stream):
@@ -265,6 +279,7 @@ def main():
         "latency_ms": {"p50": round(per_sorted[len(per) // 2], 4), "p90": round(per_sorted[int(len(per) * 0.9)], 4)},
         "fuse_context_ms": round(fuse_ms, 4),
         f"append_context_{n_app}_ms": round(append_ms, 4),
+        "decode_coords_ms": round(decode_ms, 4),
         "cold_ms_per_step": round(fuse_ms + ms, 4),
         "roofline": roof,
         "kernels": kernels,

@@ -548,4 +548,39 @@ int32_t fpd_verify_prefix(const int32_t* draft, const int32_t* target, int32_t B
   return FPD_OK;
 }
 
+int32_t fpd_coords_to_tokens(const float* values, int32_t n, double lo, double hi, int32_t coord_base,
+                             int32_t* tokens_out, void* stream) {
+  if (n < 0) return fail(FPD_E_SHAPE, "need n >= 0");
+  if (n > 0 && (!values || !tokens_out)) return fail(FPD_E_ARG, "null argument");
+  if (!(hi > lo) || !std::isfinite(lo) || !std::isfinite(hi)) return fail(FPD_E_ARG, "need finite lo < hi");
+  FPD_TRY_HIP(coords_to_tokens(values, n, lo, hi, coord_base, tokens_out, (hipStream_t)stream));
+  return FPD_OK;
+}
+
+int32_t fpd_tokens_to_coords(const int32_t* tokens, int32_t n, double lo, double hi, int32_t coord_base,
+                             double* values_out, void* stream) {
+  if (n < 0) return fail(FPD_E_SHAPE, "need n >= 0");
+  if (n > 0 && (!tokens || !values_out)) return fail(FPD_E_ARG, "null argument");
+  if (!(hi > lo) || !std::isfinite(lo) || !std::isfinite(hi)) return fail(FPD_E_ARG, "need finite lo < hi");
+  FPD_TRY_HIP(tokens_to_coords(tokens, n, lo, hi, coord_base, values_out, (hipStream_t)stream));
+  return FPD_OK;
+}
+
+int32_t fpd_ints_to_fields(const int32_t* values, int32_t n, int32_t plus_id, int32_t minus_id, int32_t digit0_id,
+                           int32_t fill_id, int32_t* fields_out, void* stream) {
+  if (n < 0) return fail(FPD_E_SHAPE, "need n >= 0");
+  if (n > 0 && (!values || !fields_out)) return fail(FPD_E_ARG, "null argument");
+  FPD_TRY_HIP(ints_to_fields(values, n, plus_id, minus_id, digit0_id, fill_id, fields_out, (hipStream_t)stream));
+  return FPD_OK;
+}
+
+int32_t fpd_fields_to_ints(const int32_t* fields, int32_t n, int32_t plus_id, int32_t minus_id, int32_t digit0_id,
+                           int32_t fill_id, int32_t* values_out, int32_t* valid_out, void* stream) {
+  if (n < 0) return fail(FPD_E_SHAPE, "need n >= 0");
+  if (n > 0 && (!fields || !values_out || !valid_out)) return fail(FPD_E_ARG, "null argument");
+  FPD_TRY_HIP(fields_to_ints(fields, n, plus_id, minus_id, digit0_id, fill_id, values_out, valid_out,
+                             (hipStream_t)stream));
+  return FPD_OK;
+}
+
 }  // extern "C"

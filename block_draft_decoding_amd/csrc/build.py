@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 SOURCES = ["api.cpp", "layout.cpp", "gemm.hip", "attention.hip", "elementwise.hip", "lmhead.hip",
-           "accept.hip", "profile.cpp"]
+           "accept.hip", "codec.hip", "profile.cpp"]
 OUT = os.path.join(PKG, "libfpd.so")
 
 
@@ -23,7 +23,7 @@ def hipcc() -> str:
 
 FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Wno-unused-result", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-ffp-contract=fast"]
+         "-ffp-contract=fast-honor-pragmas"]
 
 
 def build(verbose: bool = False) -> str:

@@ -187,4 +187,12 @@ hipError_t verify_prefix(const int32_t* draft, const int32_t* target, int B, int
 hipError_t gather_rows(int dt, const void* W, int H, const int32_t* ids, int n, void* out,
                        hipStream_t st);
 
+// ---- coordinate codec (codec.hip) -------------------------------------------------
+hipError_t coords_to_tokens(const float* x, int n, double lo, double hi, int base, int32_t* out, hipStream_t st);
+hipError_t tokens_to_coords(const int32_t* t, int n, double lo, double hi, int base, double* out, hipStream_t st);
+hipError_t ints_to_fields(const int32_t* v, int n, int plus_id, int minus_id, int digit0_id, int fill_id,
+                          int32_t* out, hipStream_t st);
+hipError_t fields_to_ints(const int32_t* f, int n, int plus_id, int minus_id, int digit0_id, int fill_id,
+                          int32_t* vals, int32_t* ok, hipStream_t st);
+
 }  // namespace fpd

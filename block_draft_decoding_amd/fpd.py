@@ -92,6 +92,11 @@ _draft_shared = _proto("fpd_draft_blocks_shared_ctx", [vp, vp, i32, i32, vp, vp,
 _argmax = _proto("fpd_constrained_argmax", [vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, vp])
 _validate = _proto("fpd_validate_primitive", [vp, vp, i32, vp, vp, vp])
 _verify = _proto("fpd_verify_prefix", [vp, vp, i32, i32, vp, vp, vp])
+f64 = ctypes.c_double
+_c2t = _proto("fpd_coords_to_tokens", [vp, i32, f64, f64, i32, vp, vp])
+_t2c = _proto("fpd_tokens_to_coords", [vp, i32, f64, f64, i32, vp, vp])
+_i2f = _proto("fpd_ints_to_fields", [vp, i32, i32, i32, i32, i32, vp, vp])
+_f2i = _proto("fpd_fields_to_ints", [vp, i32, i32, i32, i32, i32, vp, vp, vp])
 
 
 class FpdError(RuntimeError):
@@ -367,6 +372,37 @@ def fpd_verify_prefix(draft: torch.Tensor, target: torch.Tensor, k_out: torch.Te
     _check(_verify(_ptr(draft, "draft", torch.int32), _ptr(target, "target", torch.int32), B, L,
                    _ptr(k_out, "k_out", torch.int32), _ptr(next_out, "next_out", torch.int32), _stream(stream)),
            "fpd_verify_prefix")
+
+
+# ---- coordinate codec ---------------------------------------------------------------
+
+def fpd_coords_to_tokens(values: torch.Tensor, tokens_out: torch.Tensor, coord_base: int, lo: float = 0.0,
+                         hi: float = 1000.0, stream=None) -> None:
+    n = values.numel()
+    _check(_c2t(_ptr(values, "values", torch.float32), n, lo, hi, coord_base,
+                _ptr(tokens_out, "tokens_out", torch.int32), _stream(stream)), "fpd_coords_to_tokens")
+
+
+def fpd_tokens_to_coords(tokens: torch.Tensor, values_out: torch.Tensor, coord_base: int, lo: float = 0.0,
+                         hi: float = 1000.0, stream=None) -> None:
+    n = tokens.numel()
+    _check(_t2c(_ptr(tokens, "tokens", torch.int32), n, lo, hi, coord_base,
+                _ptr(values_out, "values_out", torch.float64), _stream(stream)), "fpd_tokens_to_coords")
+
+
+def fpd_ints_to_fields(values: torch.Tensor, fields_out: torch.Tensor, plus_id: int, minus_id: int,
+                       digit0_id: int, fill_id: int, stream=None) -> None:
+    n = values.numel()
+    _check(_i2f(_ptr(values, "values", torch.int32), n, plus_id, minus_id, digit0_id, fill_id,
+                _ptr(fields_out, "fields_out", torch.int32), _stream(stream)), "fpd_ints_to_fields")
+
+
+def fpd_fields_to_ints(fields: torch.Tensor, values_out: torch.Tensor, valid_out: torch.Tensor, plus_id: int,
+                       minus_id: int, digit0_id: int, fill_id: int, stream=None) -> None:
+    n = fields.numel() // 6
+    _check(_f2i(_ptr(fields, "fields", torch.int32), n, plus_id, minus_id, digit0_id, fill_id,
+                _ptr(values_out, "values_out", torch.int32), _ptr(valid_out, "valid_out", torch.int32),
+                _stream(stream)), "fpd_fields_to_ints")
 
 
 # ---- device upload of host arrays -------------------------------------------------

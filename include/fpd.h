@@ -285,6 +285,40 @@ int32_t fpd_validate_primitive(const fpd_layout *lay, const int32_t *tokens, int
 int32_t fpd_verify_prefix(const int32_t *draft, const int32_t *target, int32_t B, int32_t L,
                           int32_t *k_out, int32_t *next_out, void *stream);
 
+/* ---- coordinate codec (VFlash paper §2.3 "Token representation"; §3.1
+ * "Base VLM") ------------------------------------------------------------
+ * A coordinate occupies one of 1,001 tokens coord_base .. coord_base+1000:
+ * 2D image coordinates are normalised to 0..1000 (lo 0, hi 1000), 3D
+ * coordinates are quantised uniformly over a predefined range [lo, hi] (its
+ * values are not printed, so it is a parameter).  All device arrays, n
+ * entries, stream-ordered; nothing allocates.                              */
+
+/* bin = clamp(round-half-even((x - lo) * (1000 / (hi - lo))), 0, 1000)
+ * computed in double precision; tokens_out = coord_base + bin, or -1 for a
+ * NaN value.  values float [n].  Needs finite lo < hi.                     */
+int32_t fpd_coords_to_tokens(const float *values, int32_t n, double lo, double hi, int32_t coord_base,
+                             int32_t *tokens_out, void *stream);
+
+/* values_out double [n] = lo + bin * ((hi - lo) / 1000) for a coordinate
+ * token (bin = token - coord_base in 0..1000), NaN for any other token.    */
+int32_t fpd_tokens_to_coords(const int32_t *tokens, int32_t n, double lo, double hi, int32_t coord_base,
+                             double *values_out, void *stream);
+
+/* Fixed-width numeric fields (VFlash paper §2.3): values int32 [n] ->
+ * fields_out int32 [n, 6] = sign (plus_id for n >= 0, minus_id below), then
+ * |n| as five decimal digits (digit0_id + d) whose leading zeros, except the
+ * last digit, are fill_id.  |n| > 99,999 does not fit: six -1 tokens.      */
+int32_t fpd_ints_to_fields(const int32_t *values, int32_t n, int32_t plus_id, int32_t minus_id,
+                           int32_t digit0_id, int32_t fill_id, int32_t *fields_out, void *stream);
+
+/* Inverse: fields int32 [n, 6] -> values_out [n] and valid_out [n] (1 when
+ * the sign slot holds plus_id / minus_id and the digits read
+ * fill^j digit^(5-j) with j <= 4, the field rule of the validator; invalid
+ * fields give value 0).                                                    */
+int32_t fpd_fields_to_ints(const int32_t *fields, int32_t n, int32_t plus_id, int32_t minus_id,
+                           int32_t digit0_id, int32_t fill_id, int32_t *values_out, int32_t *valid_out,
+                           void *stream);
+
 /* ---- diagnostics -------------------------------------------------------- */
 const char *fpd_status_string(int32_t status);
 const char *fpd_last_error(void);

@@ -59,7 +59,11 @@ in the repository's design notes):
       written at cache rows pos0.. (cache row = target position);
   R23 several primitives from one observation: blocks of one length, each
       with its own anchor, attend to one shared context and to their own
-      block only (no attention between blocks).
+      block only (no attention between blocks);
+  R24 coordinate codec: bin = clamp(round-half-even((x - lo) * s), 0, 1000)
+      with s = 1000 / (hi - lo) (2D: lo 0, hi 1000, s = 1; 3D: the
+      predefined range, a parameter since its values are not printed); a bin
+      decodes to lo + bin * (hi - lo) / 1000; fields hold |n| <= 99,999.
 
 Functions whose result has no independent pin say so in their docstring.
 """
@@ -541,6 +545,78 @@ def verify_prefix(draft: np.ndarray, target: np.ndarray):
 # ---------------------------------------------------------------------------
 # whole block
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# coordinate codec (VFlash paper §2.3; §3.1 "Base VLM") -- R24, R12
+# ---------------------------------------------------------------------------
+
+N_COORD = 1001   # coordinate tokens per axis
+
+
+def coords_to_tokens(values, coord_base: int, lo: float = 0.0, hi: float = 1000.0) -> np.ndarray:
+    """Coordinate value -> one of the 1,001 coordinate tokens (R24).  2D
+    image coordinates are already normalised to 0..1000 (lo 0, hi 1000); 3D
+    coordinates are quantised uniformly over the predefined range [lo, hi].
+    bin = clamp(round_half_even((x - lo) * s), 0, 1000) with the scale
+    s = 1000 / (hi - lo) (exactly 1 for the 2D range); a NaN value gives -1."""
+    x = np.asarray(values, F64)
+    scale = F64(N_COORD - 1) / (F64(hi) - F64(lo))
+    t = (x - F64(lo)) * scale
+    b = np.clip(np.rint(t), 0, N_COORD - 1)
+    out = np.where(np.isnan(x), -1, coord_base + np.nan_to_num(b)).astype(np.int32)
+    return out
+
+
+def tokens_to_coords(tokens, coord_base: int, lo: float = 0.0, hi: float = 1000.0) -> np.ndarray:
+    """Coordinate token -> the value of its bin, lo + i * w with the bin
+    width w = (hi - lo) / 1000, for i = token - coord_base in 0..1000; NaN
+    for any other token (R24)."""
+    t = np.asarray(tokens, np.int64)
+    i = t - coord_base
+    ok = (i >= 0) & (i < N_COORD)
+    width = (F64(hi) - F64(lo)) / F64(N_COORD - 1)
+    v = F64(lo) + i.astype(F64) * width
+    return np.where(ok, v, np.nan)
+
+
+def ints_to_fields(values, plus_id: int, minus_id: int, digit0_id: int, fill_id: int) -> np.ndarray:
+    """Integer -> a fixed-width field of a sign and five digit positions
+    [n, 6] (VFlash paper §2.3): sign PLUS for n >= 0 else MINUS; |n| written
+    with five digits whose leading zeros become FILL, except the last digit
+    (R12: FILL^j DIGIT^(5-j), j <= 4).  A value with |n| > 99,999 does not
+    fit and gives six -1 tokens."""
+    v = np.asarray(values, np.int64)
+    out = np.empty(v.shape + (6,), np.int32)
+    out[..., 0] = np.where(v < 0, minus_id, plus_id)
+    a = np.abs(v)
+    for j in range(5):                       # most significant digit first
+        d = (a // 10 ** (4 - j)) % 10
+        lead = a < 10 ** (4 - j)             # nothing but zeros so far
+        out[..., 1 + j] = np.where(lead & (j < 4), fill_id, digit0_id + d)
+    out[np.abs(v) > 99_999] = -1
+    return out
+
+
+def fields_to_ints(fields, plus_id: int, minus_id: int, digit0_id: int, fill_id: int):
+    """Inverse of ints_to_fields on [n, 6] tokens.  Returns (values [n],
+    valid [n]): a field is valid when its sign is PLUS or MINUS and its digits
+    read FILL^j DIGIT^(5-j) with j <= 4 (R12); invalid fields give 0."""
+    f = np.asarray(fields, np.int64).reshape(-1, 6)
+    n = f.shape[0]
+    vals = np.zeros(n, np.int32)
+    valid = np.zeros(n, np.int32)
+    digits = set(range(digit0_id, digit0_id + 10))
+    for r in range(n):
+        sgn = f[r, 0]
+        if sgn not in (plus_id, minus_id) or _field_first_bad(f[r, 1:], fill_id, digits) >= 0:
+            continue
+        a = 0
+        for t in f[r, 1:]:
+            a = a * 10 + (int(t) - digit0_id if int(t) in digits else 0)
+        vals[r] = -a if sgn == minus_id else a
+        valid[r] = 1
+    return vals, valid
+
 
 def run_block(m: Model, feats, tokens, schema: Dict, targets=None, ctx_pos0: int = 0,
               block_pos: Optional[int] = None, want_logits: bool = False, shared_ctx: bool = False):

@@ -151,6 +151,13 @@ def test_hot_calls_reject_bad_arguments_without_gpu_work():
         assert fpd._draft(h, 8, 1, 16, 8, 8, 64, 64, 64, 8, 8, 16, None) == fpd.FPD_E_WORKSPACE
         assert fpd._argmax(h, None, 8, 1, 8, None, 8, 1 << 20, None) == fpd.FPD_E_ARG
         assert fpd._verify(8, 8, 1, 1, 8, 8, None) == fpd.FPD_E_SHAPE
+        # coordinate codec: empty ranges, negative counts, null arrays
+        assert fpd._c2t(8, 4, 5.0, 5.0, 0, 8, None) == fpd.FPD_E_ARG
+        assert fpd._c2t(8, 4, 0.0, float("inf"), 0, 8, None) == fpd.FPD_E_ARG
+        assert fpd._t2c(8, -1, 0.0, 1.0, 0, 8, None) == fpd.FPD_E_SHAPE
+        assert fpd._i2f(None, 3, 1, 2, 3, 4, 8, None) == fpd.FPD_E_ARG
+        assert fpd._f2i(8, 3, 1, 2, 3, 4, 8, None, None) == fpd.FPD_E_ARG
+        assert fpd._c2t(None, 0, 0.0, 1.0, 0, None, None) == fpd.FPD_OK  # nothing to do
         assert fpd._validate(None, 8, 1, 8, 8, None) == fpd.FPD_E_ARG
     finally:
         fpd._destroy(h)
