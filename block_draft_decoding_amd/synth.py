@@ -96,7 +96,7 @@ def schema_block_len(schema: Dict) -> int:
     kind = schema["kind"]
     if kind in ("text", "custom"):
         return int(schema["block_len"])
-    per_point = {"traj2d": 3, "traj2d3d": 6, "points3d_text": 19}[kind]
+    per_point = {"traj2d": 3, "traj2d3d": 6, "points3d_text": 19, "boxes2d": 5}[kind]
     return 1 + per_point * int(schema["n_points"])
 
 

@@ -63,7 +63,13 @@ in the repository's design notes):
   R24 coordinate codec: bin = clamp(round-half-even((x - lo) * s), 0, 1000)
       with s = 1000 / (hi - lo) (2D: lo 0, hi 1000, s = 1; 3D: the
       predefined range, a parameter since its values are not printed); a bin
-      decodes to lo + bin * (hi - lo) / 1000; fields hold |n| <= 99,999.
+      decodes to lo + bin * (hi - lo) / 1000; fields hold |n| <= 99,999;
+  R25 box acceptance: a box is [x1, y1, x2, y2, DELIM]; an external
+      confidence per drafted position is given, and a coordinate position
+      (legal set inside the coordinate ids, OFF allowed) is uncertain when
+      its confidence is not >= tau (NaN is uncertain); the drafts kept are
+      those before the first uncertain coordinate and before the first
+      schema failure, k = min(first_uncertain, first_invalid), L-1 if none.
 
 Functions whose result has no independent pin say so in their docstring.
 """
@@ -319,8 +325,9 @@ class Layout:
     coordinates.  fields: (p_first_digit, 5) for each numeric field.
     Sets are numbered in order of first appearance along the block."""
 
-    def __init__(self, L, pos_set, sets, pairs, fields, off_id, fill_id, digit_ids, vocab):
+    def __init__(self, L, pos_set, sets, pairs, fields, off_id, fill_id, digit_ids, vocab, coord_range=(0, 0)):
         self.L = L
+        self.coord_range = (int(coord_range[0]), int(coord_range[1]))   # (first coordinate id, count)
         self.pos_set = np.asarray(pos_set, np.int32)
         self.sets = [np.asarray(s, np.int64) for s in sets]
         self.pairs = [tuple(p) for p in pairs]
@@ -338,6 +345,18 @@ class Layout:
             raise ValueError("position 0 is the anchor and has no legal set")
         return self.sets[s]
 
+    def is_coord(self, p: int) -> bool:
+        """Position p holds a coordinate: its legal set is non-empty, every id
+        in it is a coordinate id or OFF, and at least one is a coordinate id
+        (R25)."""
+        s = int(self.pos_set[p])
+        if s < 0:
+            return False
+        lo, n = self.coord_range
+        ids = self.sets[s]
+        coord = (ids >= lo) & (ids < lo + n)
+        return bool(coord.any()) and bool(np.all(coord | (ids == self.off_id)))
+
     def csr(self):
         offs = np.zeros(len(self.sets) + 1, np.int32)
         for i, s in enumerate(self.sets):
@@ -352,6 +371,7 @@ def build_layout(schema: Dict, vocab: int) -> Layout:
       traj2d        [x, y, DELIM] per waypoint;
       traj2d3d      [u, v, X, Y, Z, DELIM] per waypoint, (u, v) paired when
                     an OFF id is declared, u and v then also allow OFF;
+      boxes2d       [x1, y1, x2, y2, DELIM] per box (R25);
       points3d_text ([SIGN, D, D, D, D, D] x 3 axes, DELIM) per point;
       text          every position free;
       custom        explicit sets and per-position indices."""
@@ -374,6 +394,9 @@ def build_layout(schema: Dict, vocab: int) -> Layout:
             if off >= 0:
                 pairs.append((p, p + 1))
             roles += [img, img, coords, coords, coords, (schema["delim_id"],)]
+    elif kind == "boxes2d":
+        for _ in range(schema["n_points"]):
+            roles += [coords] * 4 + [(schema["delim_id"],)]
     elif kind == "points3d_text":
         sign = tuple(sorted((schema["plus_id"], schema["minus_id"])))
         dig = tuple(sorted(digits + (schema["fill_id"],)))
@@ -390,7 +413,8 @@ def build_layout(schema: Dict, vocab: int) -> Layout:
         if len(ps) != L or ps[0] != -2:
             raise ValueError("custom pos_set must have L entries and start with -2")
         lay = Layout(L, ps, given, schema.get("pairs", []), schema.get("fields", []), off,
-                     schema.get("fill_id", -1), digits, vocab)
+                     schema.get("fill_id", -1), digits, vocab,
+                     coord_range=(schema.get("coord_base", 0), schema.get("coord_count", 0)))
         return lay
     else:
         raise ValueError(f"unknown schema kind {kind!r}")
@@ -406,7 +430,8 @@ def build_layout(schema: Dict, vocab: int) -> Layout:
             index[r] = len(sets)
             sets.append(r)
         pos_set.append(index[r])
-    return Layout(L, pos_set, sets, pairs, fields, off, schema.get("fill_id", -1), digits, vocab)
+    return Layout(L, pos_set, sets, pairs, fields, off, schema.get("fill_id", -1), digits, vocab,
+                  coord_range=(schema["coord_base"], schema["coord_count"]))
 
 
 # ---------------------------------------------------------------------------
@@ -521,6 +546,31 @@ def validate_primitive(tokens: np.ndarray, lay: Layout):
         else:
             k[b] = P
     return k, first
+
+
+def accept_boxes(tokens: np.ndarray, conf: np.ndarray, tau: float, lay: Layout):
+    """Box partial acceptance (VFlash paper §2.5: for boxes, the positions
+    before the first uncertain coordinate are kept; R25).  tokens, conf:
+    [B, L-1] (conf float32, one value per drafted position; only coordinate
+    positions are read).  Returns (k [B], first_invalid [B], first_uncertain
+    [B]); the last two are -1 when there is none."""
+    tokens = np.asarray(tokens)
+    conf = np.asarray(conf, np.float32)
+    B, P = tokens.shape
+    _, first_invalid = validate_primitive(tokens, lay)
+    tau32 = np.float32(tau)
+    k = np.full(B, P, np.int32)
+    first_unc = np.full(B, -1, np.int32)
+    coord_pos = [p for p in range(1, lay.L) if lay.is_coord(p)]
+    for b in range(B):
+        for p in coord_pos:
+            if not conf[b, p - 1] >= tau32:          # NaN is uncertain
+                first_unc[b] = p - 1
+                break
+        stops = [i for i in (first_invalid[b], first_unc[b]) if i >= 0]
+        if stops:
+            k[b] = min(stops)
+    return k, first_invalid, first_unc
 
 
 def verify_prefix(draft: np.ndarray, target: np.ndarray):
