@@ -3,8 +3,10 @@
 
 A step is one drafted block: fpd_draft_block (embedding, 5 non-causal
 GQA + SwiGLU layers, final norm) + fpd_constrained_argmax (legal-row LM
-head, masked argmax, off-frame pairing) + acceptance (schema validator, or
-prefix verification for text blocks), with the fused context K/V resident
+head, masked argmax, off-frame pairing) + acceptance (schema validator;
+prefix verification for text blocks; for box lists the validator plus the
+first uncertain coordinate of a per-position confidence vector that stands
+in for the external spatial-confidence model), with the fused context K/V resident
 in HBM.  Context fusion (fpd_fuse_context_kv) runs once per context and is
 timed and reported separately.  The default workload is the 64-waypoint
 2D+3D trajectory primitive (L = 385, context 4,096, bf16, batch 1).
@@ -27,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+BOX_TAU = 0.004             # confidence threshold of the box workloads' acceptance
 
 
 def kernel_work(tag, s, B, L, C, lay_info):
@@ -58,6 +61,7 @@ def cpu_baseline(wl, inp, budget_s):
     """The oracle's warm block (layers, full-vocabulary logits, masked argmax,
     pairing, acceptance) on the host cores; context fusion done beforehand."""
     import numpy as np
+    from block_draft_decoding_amd import synth
     from oracle import fpd_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -78,6 +82,8 @@ def cpu_baseline(wl, inp, budget_s):
         toks = O.constrained_tokens(z, lay)
         if wl.schema["kind"] == "text":
             O.verify_prefix(toks, np.zeros((toks.shape[0], toks.shape[1] + 1), np.int32))
+        elif wl.schema["kind"] == "boxes2d":
+            O.accept_boxes(toks, synth.make_box_conf(wl.batch, lay.L - 1, 4000 + wl.seed_index), BOX_TAU, lay)
         else:
             O.validate_primitive(toks, lay)
         times.append(time.time() - t)
@@ -140,6 +146,10 @@ def main():
     k_out = torch.empty(B, dtype=torch.int32, device="cuda")
     aux = torch.empty(B, dtype=torch.int32, device="cuda")
     text = wl.schema["kind"] == "text"
+    boxes = wl.schema["kind"] == "boxes2d"
+    if boxes:
+        conf = torch.from_numpy(synth.make_box_conf(B, L - 1, 4000 + wl.seed_index)).cuda()
+        unc = torch.empty(B, dtype=torch.int32, device="cuda")
     stream = torch.cuda.Stream()
     setup_s = time.time() - t0
 
@@ -157,6 +167,8 @@ def main():
         fpd.fpd_constrained_argmax(d, lay, hidden, toks, ws, stream=stream)
         if text:
             fpd.fpd_verify_prefix(toks, target, k_out, aux, stream=stream)
+        elif boxes:
+            fpd.fpd_accept_boxes(lay, toks, conf, BOX_TAU, k_out, aux, unc, stream=stream)
         else:
             fpd.fpd_validate_primitive(lay, toks, k_out, aux, stream=stream)
 
@@ -281,6 +293,7 @@ def main():
         f"append_context_{n_app}_ms": round(append_ms, 4),
         "decode_coords_ms": round(decode_ms, 4),
         "cold_ms_per_step": round(fuse_ms + ms, 4),
+        "accepted_k": k_out[:8].tolist(),
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

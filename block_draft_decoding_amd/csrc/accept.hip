@@ -36,7 +36,7 @@ constexpr int kValThreads = 512;
 
 __global__ __launch_bounds__(kValThreads) void validate_kernel(ValidateArgs a, int stage_tok, int stage_ids) {
   extern __shared__ int32_t sm[];
-  __shared__ int red[kValThreads / 64];
+  __shared__ int red[2][kValThreads / 64];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int P = a.L - 1;
   const int32_t* gtok = a.tokens + (size_t)b * P;
@@ -52,9 +52,11 @@ __global__ __launch_bounds__(kValThreads) void validate_kernel(ValidateArgs a, i
     ids = sid;
   }
   __syncthreads();
-  int first = INT_MAX;
+  int first = INT_MAX, unc = INT_MAX;
   for (int p = tid + 1; p < a.L; p += kValThreads) {
     const int t = tok[p - 1];
+    // a coordinate is certain only if its confidence reaches tau (NaN fails)
+    if (a.conf && a.coord[p] && !(a.conf[(size_t)b * P + p - 1] >= a.tau)) unc = min(unc, p - 1);
     const int s = a.pos_set[p];
     bool ok;
     if (s == -1)
@@ -81,14 +83,27 @@ __global__ __launch_bounds__(kValThreads) void validate_kernel(ValidateArgs a, i
     }
   }
   first = wave_min(first);
-  if ((tid & 63) == 0) red[tid >> 6] = first;
+  unc = wave_min(unc);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = first;
+    red[1][tid >> 6] = unc;
+  }
   __syncthreads();
   if (tid == 0) {
-    int f = red[0];
+    int f = red[0][0], u = red[1][0];
 #pragma unroll
-    for (int i = 1; i < kValThreads / 64; ++i) f = min(f, red[i]);
+    for (int i = 1; i < kValThreads / 64; ++i) {
+      f = min(f, red[0][i]);
+      u = min(u, red[1][i]);
+    }
     a.first_out[b] = f == INT_MAX ? -1 : f;
-    a.k_out[b] = f == INT_MAX ? P : 0;
+    if (a.conf) {  // keep the drafts before the first failure of either kind
+      a.uncertain_out[b] = u == INT_MAX ? -1 : u;
+      const int k = min(f, u);
+      a.k_out[b] = k == INT_MAX ? P : k;
+    } else {
+      a.k_out[b] = f == INT_MAX ? P : 0;
+    }
   }
 }
 

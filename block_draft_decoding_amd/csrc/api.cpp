@@ -48,7 +48,7 @@ struct fpd_layout {
   int32_t* dev = nullptr;  // all integer tables
   void* wg = nullptr;      // gathered legal W_lm rows [n_set_ids, H]
   // device table pointers (into dev)
-  int32_t *pos_set, *set_offsets, *set_ids, *partner, *field_w, *row_cols, *set_pos;
+  int32_t *pos_set, *set_offsets, *set_ids, *partner, *field_w, *row_cols, *set_pos, *coord;
   std::vector<int32_t> set_pos_off;  // [n_sets + 2]: positions of set s, then free positions
   std::vector<int32_t> off_col;      // [n_sets]
 };
@@ -298,7 +298,8 @@ int32_t fpd_layout_create(const fpd_drafter* d, const fpd_schema* s, fpd_layout*
     return o;
   };
   const size_t o_pos = put(h.pos_set), o_off = put(h.set_offsets), o_ids = put(h.set_ids),
-               o_par = put(partner), o_fw = put(field_w), o_rc = put(row_cols), o_sp = put(set_pos);
+               o_par = put(partner), o_fw = put(field_w), o_rc = put(row_cols), o_sp = put(set_pos),
+               o_co = put(h.coord);
   hipError_t e = hipMalloc((void**)&lay->dev, all.size() * sizeof(int32_t));
   if (e == hipSuccess) e = hipMemcpy(lay->dev, all.data(), all.size() * sizeof(int32_t), hipMemcpyHostToDevice);
   const size_t nid = h.set_ids.size(), H = d->cfg.hidden;
@@ -311,6 +312,7 @@ int32_t fpd_layout_create(const fpd_drafter* d, const fpd_schema* s, fpd_layout*
     lay->field_w = lay->dev + o_fw;
     lay->row_cols = lay->dev + o_rc;
     lay->set_pos = lay->dev + o_sp;
+    lay->coord = lay->dev + o_co;
     if (nid > 0) e = gather_rows(d->cfg.dtype, d->w.w_lm, (int)H, lay->set_ids, (int)nid, lay->wg, nullptr);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -525,10 +527,9 @@ int32_t fpd_constrained_argmax(const fpd_drafter* d, const fpd_layout* lay, cons
   return FPD_OK;
 }
 
-int32_t fpd_validate_primitive(const fpd_layout* lay, const int32_t* tokens, int32_t B, int32_t* k_out,
-                               int32_t* first_invalid_out, void* stream) {
-  if (!lay || !tokens || !k_out || !first_invalid_out) return fail(FPD_E_ARG, "null argument");
-  if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+namespace {
+ValidateArgs validate_args(const fpd_layout* lay, const int32_t* tokens, int32_t B, int32_t* k_out,
+                           int32_t* first_invalid_out) {
   const HostLayout& h = lay->host;
   ValidateArgs a{};
   a.tokens = tokens, a.pos_set = lay->pos_set, a.set_offsets = lay->set_offsets, a.set_ids = lay->set_ids;
@@ -536,6 +537,26 @@ int32_t fpd_validate_primitive(const fpd_layout* lay, const int32_t* tokens, int
   a.partner = lay->partner, a.field_w = lay->field_w;
   a.B = B, a.L = h.L, a.vocab = h.vocab, a.off_id = h.off_id, a.fill_id = h.fill_id, a.digit0_id = h.digit0_id;
   a.k_out = k_out, a.first_out = first_invalid_out;
+  return a;
+}
+}  // namespace
+
+int32_t fpd_validate_primitive(const fpd_layout* lay, const int32_t* tokens, int32_t B, int32_t* k_out,
+                               int32_t* first_invalid_out, void* stream) {
+  if (!lay || !tokens || !k_out || !first_invalid_out) return fail(FPD_E_ARG, "null argument");
+  if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+  FPD_TRY_HIP(validate_primitive(validate_args(lay, tokens, B, k_out, first_invalid_out), (hipStream_t)stream));
+  return FPD_OK;
+}
+
+int32_t fpd_accept_boxes(const fpd_layout* lay, const int32_t* tokens, const float* conf, float tau, int32_t B,
+                         int32_t* k_out, int32_t* first_invalid_out, int32_t* first_uncertain_out, void* stream) {
+  if (!lay || !tokens || !conf || !k_out || !first_invalid_out || !first_uncertain_out)
+    return fail(FPD_E_ARG, "null argument");
+  if (std::isnan(tau)) return fail(FPD_E_ARG, "tau is NaN");
+  if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+  ValidateArgs a = validate_args(lay, tokens, B, k_out, first_invalid_out);
+  a.conf = conf, a.coord = lay->coord, a.tau = tau, a.uncertain_out = first_uncertain_out;
   FPD_TRY_HIP(validate_primitive(a, (hipStream_t)stream));
   return FPD_OK;
 }

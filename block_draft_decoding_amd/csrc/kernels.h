@@ -180,6 +180,11 @@ struct ValidateArgs {
   int B, L, vocab, off_id, fill_id, digit0_id;
   int32_t* k_out;
   int32_t* first_out;
+  // box partial acceptance (optional: conf == nullptr gives all or nothing)
+  const float* conf;         // [B, L-1]
+  const int32_t* coord;      // [L]: 1 at coordinate positions
+  float tau;
+  int32_t* uncertain_out;    // [B]
 };
 hipError_t validate_primitive(const ValidateArgs& a, hipStream_t st);
 hipError_t verify_prefix(const int32_t* draft, const int32_t* target, int B, int L, int32_t* k_out,

@@ -87,6 +87,7 @@ int32_t expand_schema(const fpd_schema& s, int32_t vocab, HostLayout* out, std::
     }
     case FPD_SCHEMA_TRAJ2D:
     case FPD_SCHEMA_TRAJ2D3D:
+    case FPD_SCHEMA_BOXES2D:
     case FPD_SCHEMA_POINTS3D_TEXT: {
       if (s.n_points < 1) return need(fail(err, "n_points must be >= 1"));
       if (!check_id(s.delim_id, vocab, "delimiter", err)) return FPD_E_SCHEMA;
@@ -102,6 +103,12 @@ int32_t expand_schema(const fpd_schema& s, int32_t vocab, HostLayout* out, std::
         for (int32_t i = 0; i < s.n_points; ++i) {
           b.add(c);
           b.add(c);
+          b.add(delim);
+        }
+      } else if (s.kind == FPD_SCHEMA_BOXES2D) {
+        const Set c = coords();
+        for (int32_t i = 0; i < s.n_points; ++i) {
+          for (int32_t j = 0; j < 4; ++j) b.add(c);
           b.add(delim);
         }
       } else if (s.kind == FPD_SCHEMA_TRAJ2D3D) {
@@ -202,6 +209,21 @@ int32_t expand_schema(const fpd_schema& s, int32_t vocab, HostLayout* out, std::
   o.off_id = off;
   o.fill_id = s.fill_id;
   o.digit0_id = s.digit0_id;
+  // coordinate positions: every id of the legal set is a coordinate or OFF,
+  // and at least one is a coordinate
+  o.coord.assign(o.L, 0);
+  for (int32_t p = 1; p < o.L; ++p) {
+    const int32_t st = o.pos_set[p];
+    if (st < 0) continue;
+    bool any = false, only = true;
+    for (int32_t i = o.set_offsets[st]; i < o.set_offsets[st + 1]; ++i) {
+      const int32_t id = o.set_ids[i];
+      const bool c = s.coord_count > 0 && id >= s.coord_base && id - s.coord_base < s.coord_count;
+      any = any || c;
+      only = only && (c || (off >= 0 && id == off));
+    }
+    o.coord[p] = any && only;
+  }
 
   // structural checks common to every kind
   std::vector<int32_t> used(o.L, 0);

@@ -21,6 +21,7 @@ struct HostLayout {
   std::vector<int32_t> set_ids;      // ascending within each set
   std::vector<int32_t> pairs;        // [n_pairs * 2] block positions (u, v)
   std::vector<int32_t> fields;       // [n_fields * 2] (first digit position, width)
+  std::vector<int32_t> coord;        // [L]: 1 where the legal set is coordinate ids (and OFF) only
   int32_t off_id = -1, fill_id = -1, digit0_id = -1;
 
   int32_t n_sets() const { return (int32_t)set_offsets.size() - 1; }

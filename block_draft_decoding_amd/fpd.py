@@ -30,7 +30,7 @@ except OSError as e:  # pragma: no cover
 # ---- constants (mirror include/fpd.h) ---------------------------------------
 FPD_OK, FPD_E_ARG, FPD_E_SHAPE, FPD_E_DTYPE, FPD_E_SCHEMA, FPD_E_WORKSPACE, FPD_E_UNSUPPORTED, FPD_E_HIP = range(8)
 FPD_DTYPE_F32, FPD_DTYPE_BF16 = 0, 1
-SCHEMA_KINDS = {"text": 0, "traj2d": 1, "traj2d3d": 2, "points3d_text": 3, "custom": 4}
+SCHEMA_KINDS = {"text": 0, "traj2d": 1, "traj2d3d": 2, "points3d_text": 3, "custom": 4, "boxes2d": 5}
 
 i32 = ctypes.c_int32
 vp = ctypes.c_void_p
@@ -93,6 +93,7 @@ _argmax = _proto("fpd_constrained_argmax", [vp, vp, vp, i32, vp, vp, vp, ctypes.
 _validate = _proto("fpd_validate_primitive", [vp, vp, i32, vp, vp, vp])
 _verify = _proto("fpd_verify_prefix", [vp, vp, i32, i32, vp, vp, vp])
 f64 = ctypes.c_double
+_boxes = _proto("fpd_accept_boxes", [vp, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp])
 _c2t = _proto("fpd_coords_to_tokens", [vp, i32, f64, f64, i32, vp, vp])
 _t2c = _proto("fpd_tokens_to_coords", [vp, i32, f64, f64, i32, vp, vp])
 _i2f = _proto("fpd_ints_to_fields", [vp, i32, i32, i32, i32, i32, vp, vp])
@@ -364,6 +365,17 @@ def fpd_validate_primitive(lay: Layout, tokens: torch.Tensor, k_out: torch.Tenso
     _check(_validate(lay.handle, _ptr(tokens, "tokens", torch.int32), B, _ptr(k_out, "k_out", torch.int32),
                      _ptr(first_invalid_out, "first_invalid_out", torch.int32), _stream(stream)),
            "fpd_validate_primitive")
+
+
+def fpd_accept_boxes(lay: Layout, tokens: torch.Tensor, conf: torch.Tensor, tau: float, k_out: torch.Tensor,
+                     first_invalid_out: torch.Tensor, first_uncertain_out: torch.Tensor, stream=None) -> None:
+    B = tokens.shape[0]
+    if conf.shape != tokens.shape:
+        raise ValueError(f"conf must have the shape of tokens {tuple(tokens.shape)}, got {tuple(conf.shape)}")
+    _check(_boxes(lay.handle, _ptr(tokens, "tokens", torch.int32), _ptr(conf, "conf", torch.float32), tau, B,
+                  _ptr(k_out, "k_out", torch.int32), _ptr(first_invalid_out, "first_invalid_out", torch.int32),
+                  _ptr(first_uncertain_out, "first_uncertain_out", torch.int32), _stream(stream)),
+           "fpd_accept_boxes")
 
 
 def fpd_verify_prefix(draft: torch.Tensor, target: torch.Tensor, k_out: torch.Tensor, next_out: torch.Tensor,

@@ -161,6 +161,10 @@ WORKLOADS: Dict[str, Workload] = {
                                 shared_ctx=True,
                                 notes="16 NAVSIM-shaped 2D-trajectory blocks (L=25) against one shared "
                                       "context of 2048 positions: M = 400 projection rows"),
+    "boxes64": Workload("boxes64", DRAFTER_4B, batch=1, ctx=2048,
+                        schema=dict(kind="boxes2d", n_points=64, **_bf16_ids()), seed_index=9,
+                        notes="Dense200-shaped box list, 64 boxes x (x1, y1, x2, y2, delim), L=321; "
+                              "partial acceptance against an external per-coordinate confidence"),
     "points3d": Workload("points3d", DRAFTER_4B, batch=8, ctx=4096,
                          schema=dict(kind="points3d_text", n_points=128, **_bf16_ids()),
                          seed_index=5,
@@ -325,6 +329,13 @@ def plant_targets(draft: np.ndarray, k_star, vocab: int, seed: int) -> np.ndarra
             r = int(rng.integers(0, vocab - 1))
             tgt[b, k] = (int(draft[b, k]) + 1 + r) % vocab
     return tgt
+
+
+def make_box_conf(batch: int, n_drafted: int, seed: int) -> np.ndarray:
+    """Stand-in for the external spatial-confidence model's output: one
+    float32 per drafted position [B, L-1], uniform on [0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=seed, spawn_key=(3,))))
+    return rng.random((batch, n_drafted), dtype=np.float32)
 
 
 @dataclass

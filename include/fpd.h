@@ -78,6 +78,7 @@ enum { FPD_DTYPE_F32 = 0, FPD_DTYPE_BF16 = 1 };
  *                  pair decided jointly;
  *   POINTS3D_TEXT  per point ([SIGN, D, D, D, D, D] x 3, DELIM) -> L = 1 + 19n;
  *                  SIGN in {PLUS, MINUS}, D in {DIGIT0..DIGIT9, FILL};
+ *   BOXES2D        per box [x1, y1, x2, y2, DELIM] (2D image corners) -> L = 1 + 5n;
  *   CUSTOM         explicit legal sets, per-position set indices, pairs and
  *                  fields (block_len = L).                                 */
 enum {
@@ -85,7 +86,8 @@ enum {
   FPD_SCHEMA_TRAJ2D = 1,
   FPD_SCHEMA_TRAJ2D3D = 2,
   FPD_SCHEMA_POINTS3D_TEXT = 3,
-  FPD_SCHEMA_CUSTOM = 4
+  FPD_SCHEMA_CUSTOM = 4,
+  FPD_SCHEMA_BOXES2D = 5
 };
 
 /* Drafter shape.  H = hidden, heads of dim head_dim, n_q a multiple of n_kv,
@@ -276,6 +278,22 @@ int32_t fpd_constrained_argmax(const fpd_drafter *d, const fpd_layout *lay, cons
  * a field at its first out-of-pattern slot), -1 if valid.                 */
 int32_t fpd_validate_primitive(const fpd_layout *lay, const int32_t *tokens, int32_t B,
                                int32_t *k_out, int32_t *first_invalid_out, void *stream);
+
+/* Box partial acceptance (VFlash paper §2.5: the acceptance test adds an
+ * external spatial-confidence check for boxes, and the drafts before the
+ * first uncertain coordinate are kept; the rest is regenerated by the
+ * target).  tokens [B, L-1] int32; conf [B, L-1] float, one externally
+ * supplied confidence per drafted position, read only at coordinate
+ * positions (legal set inside the schema's coordinate ids, OFF allowed).  A
+ * coordinate is uncertain unless conf >= tau (NaN is uncertain).  Runs the
+ * schema validator of fpd_validate_primitive and writes first_invalid_out
+ * [B] as it does, first_uncertain_out [B] = the smallest uncertain
+ * coordinate index into tokens or -1, and k_out [B] = the smaller of the two
+ * indices that are >= 0, L-1 when both are -1.  Applies to any layout;
+ * trajectories keep their all-or-nothing rule (fpd_validate_primitive).
+ * Errors: E_ARG (null, NaN tau), E_SHAPE (B < 1).                         */
+int32_t fpd_accept_boxes(const fpd_layout *lay, const int32_t *tokens, const float *conf, float tau, int32_t B,
+                         int32_t *k_out, int32_t *first_invalid_out, int32_t *first_uncertain_out, void *stream);
 
 /* Greedy prefix verification (VFlash paper §2.1; blog "Method").  draft
  * [B, L-1] int32 = t_1..t_{L-1}; target [B, L] int32 = g_0..g_{L-1}, g_j the

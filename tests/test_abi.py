@@ -43,6 +43,7 @@ def _small_schemas():
         (dict(kind="traj2d3d", n_points=7, **{**ids, "off_id": 4081}), V),
         (dict(kind="traj2d3d", n_points=3, **ids), V),
         (dict(kind="points3d_text", n_points=4, **ids), V),
+        (dict(kind="boxes2d", n_points=3, **ids), V),
         (dict(kind="custom", block_len=9, sets=[[7, 3, 3, 5], [1], [2, 9, 4]],
               pos_set=[-2, 0, 1, -1, 2, 0, -1, 1, 2], pairs=[(1, 5)], fields=[], off_id=5,
               fill_id=-1, digit0_id=-1, coord_base=0, coord_count=0), 16),
@@ -52,7 +53,7 @@ def _small_schemas():
     return out
 
 
-@pytest.mark.parametrize("idx", range(11))
+@pytest.mark.parametrize("idx", range(len(_small_schemas())))
 def test_schema_expand_matches_oracle_layout(idx):
     schema, V = _small_schemas()[idx]
     got = fpd.fpd_schema_expand(schema, V)
@@ -74,6 +75,8 @@ def test_schema_expand_matches_oracle_layout(idx):
     (dict(kind="traj2d3d", n_points=2, off_id=3100), fpd.FPD_E_SCHEMA),         # OFF inside the coordinates
     (dict(kind="points3d_text", n_points=2, fill_id=4084), fpd.FPD_E_SCHEMA),   # fill equals a digit
     (dict(kind="text", block_len=1), fpd.FPD_E_SCHEMA),
+    (dict(kind="boxes2d", n_points=0), fpd.FPD_E_SCHEMA),
+    (dict(kind="boxes2d", n_points=2, coord_count=0), fpd.FPD_E_SCHEMA),
     (dict(kind="custom", block_len=3, sets=[[1]], pos_set=[0, 0, 0]), fpd.FPD_E_SCHEMA),
     (dict(kind="custom", block_len=3, sets=[[]], pos_set=[-2, 0, 0]), fpd.FPD_E_SCHEMA),
     (dict(kind="custom", block_len=3, sets=[[1, 2]], pos_set=[-2, 0, 0], pairs=[(1, 2)]), fpd.FPD_E_SCHEMA),
@@ -159,6 +162,10 @@ def test_hot_calls_reject_bad_arguments_without_gpu_work():
         assert fpd._f2i(8, 3, 1, 2, 3, 4, 8, None, None) == fpd.FPD_E_ARG
         assert fpd._c2t(None, 0, 0.0, 1.0, 0, None, None) == fpd.FPD_OK  # nothing to do
         assert fpd._validate(None, 8, 1, 8, 8, None) == fpd.FPD_E_ARG
+        # box acceptance: null confidences, NaN threshold, no rows (checked before the layout is read)
+        assert fpd._boxes(8, 8, None, 0.5, 1, 8, 8, 8, None) == fpd.FPD_E_ARG
+        assert fpd._boxes(8, 8, 8, float("nan"), 1, 8, 8, 8, None) == fpd.FPD_E_ARG
+        assert fpd._boxes(8, 8, 8, 0.5, 0, 8, 8, 8, None) == fpd.FPD_E_SHAPE
     finally:
         fpd._destroy(h)
 
