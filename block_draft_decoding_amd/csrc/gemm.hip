@@ -137,7 +137,13 @@ __device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, i
 // load a clamped in-range row instead of being switched off, so every wave
 // issues the same number of loads per stage and vmcnt counts stay exact; the
 // outputs of those rows/columns are never stored.
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool PAIRED, class Map, class Epi>
+//
+// When M = k BM + r with 0 < r <= XR, the last row tile also carries the r
+// leftover rows (an (XR x BK) A slab after its BM rows in each stage, filled
+// by 4-byte LDS-writing loads, multiplied by 16x16x32 MFMAs whose columns are
+// split over all waves).  A separate row tile for them would stream the whole
+// weight column once more from HBM for r rows of work.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int XR, bool PAIRED, class Map, class Epi>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, int w_rows, Map map,
     int ncols, Epi epi, float* __restrict__ partial, int part_ld, int m_tiles, int n_tiles,
@@ -155,7 +161,13 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   static_assert(!PAIRED || (TN % 2 == 0), "paired epilogues need an even number of N sub-tiles");
   static_assert(STAGES >= 2 && STAGES <= 8 && LPS * (STAGES - 1) < 64, "pipeline depth");
   constexpr int CPT = PAIRED ? BN / 2 : BN;  // logical columns per tile
-  constexpr int STAGE = (BM + BN) * CH;      // 16-byte slots per stage
+  static_assert(XR == 0 || XR == gemm_extra_rows(BM, BN, BK, NW, PAIRED), "extra rows of this tile shape");
+  constexpr int XI = XR * BK * 2 / (NW * 256);  // 4-byte loads per wave and stage for the extra rows
+  constexpr int XB = XR ? CPT / (NW * 16) : 0;  // 16-column blocks (pairs when PAIRED) per wave
+  constexpr int XA = PAIRED ? 2 * XB : XB;      // their accumulators
+  static_assert(XR == 0 || (XI >= 1 && XI * NW * 256 == XR * BK * 2 && XB * NW * 16 == CPT), "extra rows");
+  constexpr int AR = BM + XR;                // A rows held per stage
+  constexpr int STAGE = (AR + BN) * CH;      // 16-byte slots per stage
 
   __shared__ u32x4_t lds[STAGES * STAGE];
 
@@ -170,6 +182,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   const int m0 = mt * BM, c0 = nt * CPT;
   const int KT = K / BK;
   const int kt0 = (int)((long)ks * KT / splits), kt1 = (int)((long)(ks + 1) * KT / splits);
+  const bool ext = XR > 0 && m0 + BM < M;  // the last row tile carries rows BM .. BM + XR - 1
 
   // Operands are read through buffer descriptors: the per-lane byte offset
   // (row and swizzled chunk) is fixed, the K-tile offset is a scalar.  The
@@ -200,13 +213,27 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     }
     boff[i] = (uint32_t)(((size_t)wrow * K + c * 8) * 2);
   }
-  auto issue = [&](int kt, int stage) {
+  // extra rows: instruction i of a wave fills 16 slots (256 bytes); lane
+  // `lane` writes word lane % 4 of slot lane / 4
+  uint32_t xoff[XI > 0 ? XI : 1];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int q = (wave * XI + i) * 16 + lane / 4, r = BM + q / CH;
+    const int c = (q % CH) ^ ((r / (16 / CH)) & (CH - 1));
+    const int m = min(m0 + r, M - 1);
+    xoff[i] = (uint32_t)(((size_t)m * lda + c * 8) * 2 + (lane & 3) * 4);
+  }
+  auto issue = [&](int kt, int stage, auto ext_c) {
     const int soff = kt * BK * 2;
     u32x4_t* base = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < AI; ++i) lds_dma16(arsrc, base + (wave * AI + i) * 64, aoff[i], soff);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + BM * CH + (wave * BI + i) * 64, boff[i], soff);
+    for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + AR * CH + (wave * BI + i) * 64, boff[i], soff);
+    if constexpr (decltype(ext_c)::value) {
+#pragma unroll
+      for (int i = 0; i < XI; ++i) lds_dma4(arsrc, base + BM * CH + (wave * XI + i) * 16, xoff[i], soff);
+    }
   };
 
   f32x16_t acc[TM][TN];
@@ -216,6 +243,15 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  f32x4_t xacc[XA > 0 ? XA : 1];
+#pragma unroll
+  for (int b = 0; b < (XA > 0 ? XA : 1); ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xacc[b][r] = 0.f;
+  // first column (pair index when PAIRED) of this wave's extra-row blocks;
+  // block b covers xcol0 + 16 b .. + 15 (PAIRED: first members there, second
+  // members at BN / 2 + the same offset)
+  const int xcol0 = wave * 16 * XB;
 
   int bcol[TN];
 #pragma unroll
@@ -241,26 +277,41 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   // barrier then hands the finished stage back to the loads (K-tile kt +
   // STAGES goes into it) and publishes the next K-tile, whose first fragments
   // are read before the last MFMAs of the current one.
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (kt0 + s < kt1) issue(kt0 + s, s);
-
-  auto mainloop = [&](auto nr_c) {
+  auto mainloop = [&](auto nr_c, auto ext_c) {
     constexpr int NR = decltype(nr_c)::value;
+    constexpr bool EXT = decltype(ext_c)::value;
+    constexpr int LPSX = LPS + (EXT ? XI : 0);  // loads per wave and stage
     constexpr int KS = BK / 16;
     bf16x8_t af[2][TM > 0 ? TM : 1], bfv[2][TN];
+    // extra rows: fragments of the two 32-deep K steps of a K-tile (j = kk / 2)
+    bf16x8_t xa[2], xb[2][XA > 0 ? XA : 1];
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (kt0 + s < kt1) issue(kt0 + s, s, ext_c);
     auto fetch = [&](int stage, int kk, int buf) {
+      const u32x4_t* As = lds + stage * STAGE;
+      const u32x4_t* Bs = As + AR * CH;
       if constexpr (NR > 0) {
-        const u32x4_t* As = lds + stage * STAGE;
-        const u32x4_t* Bs = As + BM * CH;
 #pragma unroll
         for (int i = 0; i < NR; ++i)
           af[buf][i] = __builtin_bit_cast(bf16x8_t, As[swz<CH>(wm * WM + i * 32 + lr, kk * 2 + lk)]);
 #pragma unroll
         for (int j = 0; j < TN; ++j) bfv[buf][j] = __builtin_bit_cast(bf16x8_t, Bs[swz<CH>(bcol[j] + lr, kk * 2 + lk)]);
       }
+      if constexpr (EXT) {
+        if (kk % 2 == 0) {  // 16x16x32 operands: lane reads row/column lane % 16, K chunk lane / 16
+          const int j = kk / 2, kc = kk * 2 + (lane >> 4), r16 = lane & 15;
+          xa[j] = __builtin_bit_cast(bf16x8_t, As[swz<CH>(BM + r16, kc)]);
+#pragma unroll
+          for (int b = 0; b < XA; ++b) {
+            const int col = (PAIRED && b >= XB) ? BN / 2 + xcol0 + 16 * (b - XB) : xcol0 + 16 * b;
+            xb[j][b] = __builtin_bit_cast(bf16x8_t, Bs[swz<CH>(col + r16, kc)]);
+          }
+        }
+      }
     };
-    auto mma = [&](int buf) {
+    auto mma = [&](int kk) {
+      const int buf = kk & 1;
       if constexpr (NR > 0) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
@@ -268,10 +319,17 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfv[buf][j], acc[i][j], 0, 0, 0);
       }
+      if constexpr (EXT) {
+        if (kk % 2 == 1) {
+#pragma unroll
+          for (int b = 0; b < XA; ++b)
+            xacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[kk / 2], xb[kk / 2][b], xacc[b], 0, 0, 0);
+        }
+      }
     };
     if (kt0 >= kt1) return;
     wait_lgkm0();
-    wait_stages<LPS, STAGES - 1>(min(STAGES - 1, kt1 - 1 - kt0));
+    wait_stages<LPSX, STAGES - 1>(min(STAGES - 1, kt1 - 1 - kt0));
     barrier_nofence();
     fetch(0, 0, 0);
     for (int kt = kt0; kt < kt1; ++kt) {
@@ -282,32 +340,70 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
           fetch(stage, kk + 1, (kk + 1) & 1);
         } else {
           wait_lgkm0();
-          if (kt + 1 < kt1) wait_stages<LPS, STAGES - 2>(min(STAGES - 2, kt1 - 2 - kt));
+          if (kt + 1 < kt1) wait_stages<LPSX, STAGES - 2>(min(STAGES - 2, kt1 - 2 - kt));
           barrier_nofence();
-          if (kt + STAGES < kt1) issue(kt + STAGES, stage);
+          if (kt + STAGES < kt1) issue(kt + STAGES, stage, ext_c);
           if (kt + 1 < kt1) fetch(stage + 1 == STAGES ? 0 : stage + 1, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mma(kk & 1);
+        mma(kk);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  if (nr == TM) {
-    mainloop(std::integral_constant<int, TM>{});
+  using NoExt = std::false_type;
+  bool extended = false;
+  if constexpr (XR > 0) {
+    if (ext) {
+      mainloop(std::integral_constant<int, TM>{}, std::true_type{});
+      extended = true;
+    }
+  }
+  if (extended) {
+  } else if (nr == TM) {
+    mainloop(std::integral_constant<int, TM>{}, NoExt{});
   } else if (nr == 0) {
-    mainloop(std::integral_constant<int, 0>{});
+    mainloop(std::integral_constant<int, 0>{}, NoExt{});
   } else {
     if constexpr (TM > 1) {
       if (nr == 1)
-        mainloop(std::integral_constant<int, 1>{});
+        mainloop(std::integral_constant<int, 1>{}, NoExt{});
       else
-        mainloop(std::integral_constant<int, TM>{});
+        mainloop(std::integral_constant<int, TM>{}, NoExt{});
     }
   }
 
   // epilogue: lane holds column (lane % 32) and rows (r/4)*8 + (lane/32)*4 + r%4 of each sub-tile
   float* part = splits > 1 ? partial + (size_t)ks * M * part_ld : nullptr;
+  if constexpr (XR > 0) {
+    // extra rows (16x16 blocks): lane holds column lane % 16, rows 4 (lane / 16) + r
+    if (ext) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + BM + 4 * (lane >> 4) + r;
+        if (m >= M) continue;
+#pragma unroll
+        for (int b = 0; b < XB; ++b) {
+          const int c = c0 + xcol0 + 16 * b + (lane & 15);
+          if (c >= ncols) continue;
+          if constexpr (PAIRED) {
+            const float v0 = xacc[b][r], v1 = xacc[XB + b][r];
+            if (part) {
+              part[(size_t)m * part_ld + map.first(c)] = v0;
+              part[(size_t)m * part_ld + map.second(c)] = v1;
+            } else {
+              epi.pair(m, c, v0, v1);
+            }
+          } else {
+            if (part)
+              part[(size_t)m * part_ld + c] = xacc[b][r];
+            else
+              epi(m, c, xacc[b][r]);
+          }
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -523,8 +619,19 @@ template <int BM, int BN, int BKT, int WMW, int WNW, int S, bool PAIRED, class M
 void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, const bf16_t* w, Map map, int ncols,
                 int nw, Epi epi, float* part, hipStream_t st) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, PAIRED, Map, Epi>), dim3(grid), dim3(64 * WMW * WNW), 0,
-                     st, a, lda, M, K, w, nw, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
+  constexpr int XR = gemm_extra_rows(BM, BN, BKT, WMW * WNW, PAIRED);
+  // the extended-tile kernel only where the plan folds leftover rows into the
+  // last row tile; the plain kernel keeps its smaller code and LDS otherwise
+  if constexpr (XR > 0) {
+    if (pl.ext) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, XR, PAIRED, Map, Epi>), dim3(grid),
+                         dim3(64 * WMW * WNW), 0, st, a, lda, M, K, w, nw, map, ncols, epi, part, nw, pl.m_tiles,
+                         pl.n_tiles, pl.splits);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, 0, PAIRED, Map, Epi>), dim3(grid), dim3(64 * WMW * WNW),
+                     0, st, a, lda, M, K, w, nw, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
 }
 
 template <bool PAIRED, class Map, class Epi>
@@ -584,10 +691,10 @@ hipError_t run_f32(const void* A, int lda, int M, int K, const void* W, Map map,
 
 namespace {
 struct CfgShape {
-  int rows, cols, bk;
+  int rows, cols, bk, waves;
 };
 constexpr CfgShape kCfgShape[GEMM_NUM_CFGS] = {
-#define FPD_SHAPE(E, BM, BN, BKT, WMW, WNW, S) {BM, BN, BKT},
+#define FPD_SHAPE(E, BM, BN, BKT, WMW, WNW, S) {BM, BN, BKT, WMW * WNW},
     FPD_GEMM_CFGS(FPD_SHAPE)
 #undef FPD_SHAPE
 };
@@ -596,12 +703,20 @@ constexpr CfgShape kCfgShape[GEMM_NUM_CFGS] = {
 int gemm_cfg_rows(int cfg) { return kCfgShape[cfg].rows; }
 int gemm_cfg_cols(int cfg) { return kCfgShape[cfg].cols; }
 int gemm_cfg_bk(int cfg) { return kCfgShape[cfg].bk; }
+int gemm_cfg_extra_rows(int cfg, bool paired) {
+  const CfgShape& c = kCfgShape[cfg];
+  return gemm_extra_rows(c.rows, c.cols, c.bk, c.waves, paired);
+}
 
-GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int splits) {
+GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int splits, bool fold) {
   GemmPlan p;
   p.cfg = cfg;
   const int bm = gemm_cfg_rows(cfg), cpt = gemm_cfg_cols(cfg) / (paired ? 2 : 1);
   p.m_tiles = (M + bm - 1) / bm;
+  if (fold && M > bm && M % bm != 0 && M % bm <= gemm_cfg_extra_rows(cfg, paired)) {
+    p.m_tiles = M / bm;
+    p.ext = true;
+  }
   p.n_tiles = (ncols + cpt - 1) / cpt;
   p.splits = std::max(1, std::min(splits, K / gemm_cfg_bk(cfg)));
   p.partial_floats = p.splits > 1 ? (size_t)p.splits * M * nw : 0;
@@ -628,6 +743,11 @@ GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   if (M <= 32) return with_splits(GEMM_32x128_S4, 1024, 2048);
   if (M <= 64) return with_splits(GEMM_64x128_S3, 1024, 2048);
   const GemmPlan big = make_plan(GEMM_128x256_W8_S3, M, ncols, K, nw, paired, 1);
+  const GemmPlan folded = make_plan(GEMM_128x256_W8_S3, M, ncols, K, nw, paired, 1, /*fold=*/true);
+  // A few leftover rows would otherwise form a second wave of one-row tiles,
+  // each streaming its whole weight column again: carry them in the last
+  // full row tile instead when that keeps the grid within one pass.
+  if (folded.ext && big.m_tiles * big.n_tiles > 256 && folded.m_tiles * folded.n_tiles >= 224) return folded;
   if (big.m_tiles * big.n_tiles >= 224) return big;
   if (paired || K >= 8192) {
     const int full = M / 128, rem_blocks = (M - full * 128 + 31) / 32;  // 32-row blocks of the last tile

@@ -43,12 +43,22 @@ enum GemmCfg {
 struct GemmPlan {
   int cfg = GEMM_128x128_S2;
   int m_tiles = 1, n_tiles = 1, splits = 1;
+  bool ext = false;           // the last row tile carries the rows past (m_tiles) * BM
   size_t partial_floats = 0;  // split-K scratch (splits * M * N_w floats) when splits > 1
 };
-GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int splits);
+// Rows past BM that the last row tile of a bf16 GEMM configuration can carry
+// (so that M = k BM + r, r <= this, needs no extra row tile re-reading the
+// weights): 16 where the K tile is 64 wide, BM >= 64 and every wave gets at
+// least one 16-column block of the extra rows.
+constexpr int gemm_extra_rows(int bm, int bn, int bk, int waves, bool paired) {
+  return (bk == 64 && bm >= 64 && (paired ? bn / 2 : bn) >= waves * 16) ? 16 : 0;
+}
+// fold: let the last row tile carry up to gemm_extra_rows leftover rows
+GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int splits, bool fold = false);
 int gemm_cfg_rows(int cfg);
 int gemm_cfg_cols(int cfg);
 int gemm_cfg_bk(int cfg);
+int gemm_cfg_extra_rows(int cfg, bool paired);
 // M rows, ncols logical output columns (pairs for paired epilogues), K depth,
 // nw = W rows covered (partial row length), paired = two W rows per column.
 GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired);
