@@ -9,8 +9,9 @@ Two summaries are produced:
   (``FETCH_SIZE``, then ``WRITE_SIZE``; both report KiB per dispatch), each
   scaled by what the same counter reads for a plain device copy of known
   size (``bench.py --copy-calibration``).  The summary records a digest of
-  the library sources; bench.py reports the traffic only while the sources
-  still have that digest, i.e. while the kernel is the one measured.
+  the source files that define the measured kernel; bench.py reports the
+  traffic only while those files still have that digest, i.e. while the
+  kernel is the one measured.
 
 Command line:
   python -m block_draft_decoding_amd.profiling stats STATS_CSV OUT_MD TITLE COMMAND [BENCH_JSON]
@@ -35,12 +36,25 @@ CSRC = os.path.join(ROOT, "block_draft_decoding_amd", "csrc")
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_gate_up_traj2d3d_L385.md")
 
 
-def source_digest() -> str:
-    """sha256 over the library's kernel and host sources (sorted by name)."""
+# source files that define each kernel tag's code (its kernel, the helpers it
+# includes, and the launch plan)
+KERNEL_SOURCES = {"gemm": ("gemm.hip", "lds_pipe.h", "common.h", "kernels.h")}
+
+
+def kernel_files(tag: Optional[str]) -> Optional[tuple]:
+    if tag and tag.startswith("gemm"):
+        return KERNEL_SOURCES["gemm"]
+    return None
+
+
+def source_digest(files: Optional[tuple] = None) -> str:
+    """sha256 over the given library sources (default: all kernel and host
+    sources), sorted by name."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if os.path.splitext(p)[1] in (".hip", ".h", ".cpp"):
-            h.update(os.path.basename(p).encode())
+        name = os.path.basename(p)
+        if os.path.splitext(p)[1] in (".hip", ".h", ".cpp") and (files is None or name in files):
+            h.update(name.encode())
             with open(p, "rb") as f:
                 h.update(f.read())
     return h.hexdigest()[:16]
@@ -110,7 +124,7 @@ def traffic_summary(args) -> str:
     rec = {"tag": args.tag, "kernel_regex": args.kernel_regex, "fetch_bytes": round(fetch_b),
            "write_bytes": round(write_b), "traffic_bytes": round(fetch_b + write_b),
            "copy_factor_fetch": round(f_fetch, 4), "copy_factor_write": round(f_write, 4),
-           "source_digest": source_digest()}
+           "source_files": list(kernel_files(args.tag) or ()), "source_digest": source_digest(kernel_files(args.tag))}
     cmds = open(args.commands).read().strip() if args.commands else ""
     lines = [f"# HBM traffic of one `{args.tag}` launch (64-waypoint 2D+3D trajectory block, L=385, bf16)", "",
              "Counters from four `rocprofv3 --pmc` runs (run from the repository root on one MI355X):", "",
@@ -123,14 +137,14 @@ def traffic_summary(args) -> str:
              f"Scale factors (copy bytes / counter bytes): fetch {f_fetch:.4f}, write {f_write:.4f}.  "
              f"HBM traffic per launch: {fetch_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written = "
              f"{(fetch_b + write_b) / 1e6:.1f} MB.", "",
-             "Machine-readable record (bench.py reports `traffic` only while the library sources have this "
-             "digest):", "", "```json", json.dumps(rec), "```"]
+             "Machine-readable record (bench.py reports `traffic` only while the kernel's source files have "
+             "this digest):", "", "```json", json.dumps(rec), "```"]
     return "\n".join(lines) + "\n"
 
 
 def read_traffic(tag: str, path: str = TRAFFIC_MD) -> Optional[int]:
     """Measured HBM bytes per launch of `tag`, or None when no measurement
-    exists or the library sources changed since it was taken."""
+    exists or the kernel's source files changed since it was taken."""
     try:
         text = open(path).read()
     except OSError:
@@ -139,7 +153,7 @@ def read_traffic(tag: str, path: str = TRAFFIC_MD) -> Optional[int]:
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("tag") != tag or rec.get("source_digest") != source_digest():
+    if rec.get("tag") != tag or rec.get("source_digest") != source_digest(kernel_files(tag)):
         return None
     return int(rec["traffic_bytes"])
 
