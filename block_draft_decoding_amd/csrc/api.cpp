@@ -342,8 +342,12 @@ int32_t fpd_layout_masks(const fpd_layout* lay, fpd_layout_sizes* sizes, int32_t
 int32_t fpd_workspace_size(const fpd_drafter* d, int32_t B, int32_t C, int32_t L, size_t* bytes) {
   if (!d || !bytes) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || C < 0 || L < 2) return fail(FPD_E_SHAPE, "need B >= 1, C >= 0, L >= 2");
-  const int chunk = head_chunk_cols(d->cfg.dtype);
-  const int worst = (d->cfg.vocab + chunk - 1) / chunk;
+  // LM-head partials: wide chunks of the whole vocabulary, or narrow chunks,
+  // which are used only while the wide ones number under 128 per launch
+  // (at most 4 x 127 narrow chunks in a row)
+  const int wide = head_chunk_cols(d->cfg.dtype), narrow = head_chunk_cols(d->cfg.dtype, true);
+  const int worst = std::max((d->cfg.vocab + wide - 1) / wide,
+                             std::min((d->cfg.vocab + narrow - 1) / narrow, 4 * 127));
   size_t need = plan_draft(*d, B, L, C).total;
   if (C > 0) need = std::max(need, plan_fuse(*d, B, C).total);
   need = std::max(need, plan_head(B, L, worst).total);
@@ -491,8 +495,20 @@ int32_t fpd_constrained_argmax(const fpd_drafter* d, const fpd_layout* lay, cons
   if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
   const HostLayout& h = lay->host;
   const fpd_config& c = d->cfg;
-  const int L = h.L, ns = h.n_sets(), chunk = head_chunk_cols(c.dtype);
+  const int L = h.L, ns = h.n_sets();
+  // narrow column chunks when the wide ones would give fewer than 128 work
+  // items (each then streams ~0.8 MB through one CU); such layouts have at
+  // most 4 x 127 narrow chunks per row, within fpd_workspace_size's bound
+  long wide_items = 0;
+  for (int s2 = 0; s2 <= ns; ++s2) {
+    const int npos = lay->set_pos_off[s2 + 1] - lay->set_pos_off[s2];
+    const int ncols = s2 < ns ? h.set_offsets[s2 + 1] - h.set_offsets[s2] : c.vocab;
+    const int wide = head_chunk_cols(c.dtype);
+    wide_items += (long)((B * npos + 31) / 32) * ((ncols + wide - 1) / wide);
+  }
+  const int chunk = head_chunk_cols(c.dtype, wide_items < 128);
   HeadArgs ha{};
+  ha.chunk_cols = chunk;
   ha.hidden = hidden;
   ha.B = B, ha.L = L, ha.H = c.hidden, ha.width = h.width(), ha.logits = logits_out;
   ReduceArgs ra{};

@@ -19,6 +19,7 @@ namespace {
 constexpr int BK = 64;
 constexpr int HBM = 32;    // rows per tile (bf16)
 constexpr int HBN = 128;   // columns per chunk (bf16): 4 waves x 32
+constexpr int HBN_NARROW = 32;  // one wave: for layouts whose 128-column chunks give few work items
 constexpr int HST = 4;     // depth of the global -> LDS ring (bf16)
 constexpr int FBM = 16;    // f32 path: rows per tile
 constexpr int FBN = 64;    // f32 path: columns per chunk
@@ -58,15 +59,21 @@ __device__ __forceinline__ void wave_argmax(float& v, int& c, int width) {
 // W_lm rows stream global -> LDS through an HST-deep ring of LDS-writing
 // buffer loads (K-tile offsets are scalar; each lane's row offset is fixed),
 // so several K-tiles are in flight while the MFMAs run.  16-byte chunks are
-// bank-swizzled as in the dense GEMM.
-__global__ __launch_bounds__(256) void head_bf16_kernel(HeadArgs a) {
+// bank-swizzled as in the dense GEMM.  One wave per 32 columns of the chunk.
+template <int CN>
+__global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
+  constexpr int HW = CN / 32;                      // waves
+  constexpr int NT = 64 * HW;
   constexpr int CH = BK / 8;                       // 16-byte chunks per tile row
-  constexpr int STAGE = (HBM + HBN) * CH;          // chunks per stage
-  constexpr int BI = HBN * CH / 256;               // B loads per thread and stage (A: one)
-  constexpr int LPS = 1 + BI;
+  constexpr int STAGE = (HBM + CN) * CH;           // chunks per stage
+  constexpr int AI = HBM * CH / NT;                // A loads per thread and stage
+  constexpr int BI = CN * CH / NT;                 // B loads per thread and stage
+  constexpr int LPS = AI + BI;
+  static_assert(AI * NT == HBM * CH && BI * NT == CN * CH, "tile shape");
+  static_assert(LPS * (HST - 1) < 64, "pipeline depth");
   __shared__ u32x4_t lds[HST * STAGE];
-  __shared__ float red_v[4][HBM];
-  __shared__ int red_c[4][HBM];
+  __shared__ float red_v[HW][HBM];
+  __shared__ int red_c[HW][HBM];
   __shared__ int rowmap[HBM];  // hidden / output row of each tile row (rows past the set repeat a valid one)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,18 +82,19 @@ __global__ __launch_bounds__(256) void head_bf16_kernel(HeadArgs a) {
   if (it.set < 0) return;
   const HeadSet& S = a.sets[it.set];
   const int M = a.B * S.n_pos, H = a.H;
-  const int m0 = it.mt * HBM, c0 = it.chunk * HBN;
+  const int m0 = it.mt * HBM, c0 = it.chunk * CN;
 
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.hidden, (short)0, (int)((size_t)a.B * (a.L - 1) * H * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t brsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)S.w, (short)0, (int)((size_t)S.n_cols * H * 2), 0x00020000);
   if (tid < HBM) rowmap[tid] = set_row(a, S, min(m0 + tid, M - 1));
-  uint32_t aoff, boff[BI];
-  {
-    const int sl = wave * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
+  uint32_t aoff[AI], boff[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int sl = (wave * AI + i) * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
     const int row = set_row(a, S, min(m0 + r, M - 1));
-    aoff = (uint32_t)(((size_t)row * H + c * 8) * 2);
+    aoff[i] = (uint32_t)(((size_t)row * H + c * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
@@ -97,7 +105,8 @@ __global__ __launch_bounds__(256) void head_bf16_kernel(HeadArgs a) {
   auto issue = [&](int kt, int stage) {
     const int soff = kt * BK * 2;
     u32x4_t* base = lds + stage * STAGE;
-    lds_dma16(arsrc, base + wave * 64, aoff, soff);
+#pragma unroll
+    for (int i = 0; i < AI; ++i) lds_dma16(arsrc, base + (wave * AI + i) * 64, aoff[i], soff);
 #pragma unroll
     for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + HBM * CH + (wave * BI + i) * 64, boff[i], soff);
   };
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(256) void head_bf16_kernel(HeadArgs a) {
   if (tid < HBM) {
     float bv = red_v[0][tid];
     int bc = red_c[0][tid];
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < HW; ++w)
       if (arg_better(red_v[w][tid], red_c[w][tid], bv, bc)) {
         bv = red_v[w][tid];
         bc = red_c[w][tid];
@@ -317,7 +326,10 @@ __global__ __launch_bounds__(256) void pad_kernel(float* logits, int rows, int w
 
 }  // namespace
 
-int head_chunk_cols(int dt) { return dt == FPD_DTYPE_BF16 ? HBN : FBN; }
+int head_chunk_cols(int dt, bool narrow) {
+  if (dt != FPD_DTYPE_BF16) return FBN;
+  return narrow ? HBN_NARROW : HBN;
+}
 
 hipError_t lm_head_partials(int dt, const HeadArgs& a, hipStream_t st) {
   ProfScope prof("lm_head", st);
@@ -330,8 +342,12 @@ hipError_t lm_head_partials(int dt, const HeadArgs& a, hipStream_t st) {
   if ((size_t)a.B * (a.L - 1) * a.H * 2 > 0xffffffffull) return hipErrorInvalidValue;
   for (int s = 0; s < a.n_sets; ++s)
     if ((size_t)a.sets[s].n_cols * a.H * 2 > 0xffffffffull) return hipErrorInvalidValue;
-  if (dt == FPD_DTYPE_BF16)
-    hipLaunchKernelGGL(head_bf16_kernel, dim3((unsigned)items), dim3(256), 0, st, a);
+  if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN_NARROW)
+    hipLaunchKernelGGL(head_bf16_kernel<HBN_NARROW>, dim3((unsigned)items), dim3(2 * HBN_NARROW), 0, st, a);
+  else if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN)
+    hipLaunchKernelGGL(head_bf16_kernel<HBN>, dim3((unsigned)items), dim3(2 * HBN), 0, st, a);
+  else if (dt == FPD_DTYPE_BF16)
+    return hipErrorInvalidValue;
   else
     hipLaunchKernelGGL(head_f32_kernel, dim3((unsigned)items), dim3(256), 0, st, a);
   return hipGetLastError();

@@ -38,7 +38,7 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_gate_up_traj2d3d_L
 
 # source files that define each kernel tag's code (its kernel, the helpers it
 # includes, and the launch plan)
-KERNEL_SOURCES = {"gemm": ("gemm.hip", "lds_pipe.h", "common.h", "kernels.h")}
+KERNEL_SOURCES = {"gemm": ("gemm.hip", "gemm.h", "lds_pipe.h", "common.h")}
 
 
 def kernel_files(tag: Optional[str]) -> Optional[tuple]:
