@@ -375,9 +375,11 @@ int attn_splits(int B, int L, int C, int nq, int nkv, int* q_tiles_out, int* tot
   const int tiles = (C + KT - 1) / KT + (L + KT - 1) / KT;
   const int base = q_tiles * B * nkv;
   // one workgroup per CU: split the keys until the grid would exceed one
-  // pass over the 256 CUs (more splits only add combine traffic)
+  // pass over the 256 CUs (more splits only add combine traffic), keeping at
+  // least two key tiles per split (one-tile splits write a partial O per
+  // tile: slower on short blocks over 2,048 keys, measured)
   int splits = 1;
-  while (base * splits * 2 <= 256 && splits * 2 <= tiles && splits < 32) splits *= 2;
+  while (base * splits * 2 <= 256 && splits * 2 * 2 <= tiles && splits < 32) splits *= 2;
   if (q_tiles_out) *q_tiles_out = q_tiles;
   if (total_tiles) *total_tiles = tiles;
   return splits;

@@ -83,9 +83,8 @@ __device__ __forceinline__ void store_norm4<float>(float* dst, f32x4_t v, float 
 // rows r = b*L + l with l >= 1 produce output, at row b*(L-1) + l - 1 (the
 // drafter's final norm over the masked positions).  H is a multiple of 64
 // and at most 4096 (the row stays in registers: 4 float4 per thread).
-// NS > 0: exactly NS split-K partials, all loads issued before the sums
-// (a runtime-length loop would serialise one memory round trip per split);
-// NS = 0: `splits` partials in batches of 8.
+// Exactly NS (1..8) split-K partials, all loads issued before the sums (a
+// runtime-length loop would serialise one memory round trip per split).
 template <class T, int NS>
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict__ partial, int splits, int M, int H,
                                                          float* __restrict__ h, const T* __restrict__ g, float eps,
@@ -110,25 +109,12 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
     if (k < n4) {
       f32x4_t x = hr[k];
       if (pr) {
-        f32x4_t acc;
-        if constexpr (NS > 0) {
-          f32x4_t parts[NS];
+        f32x4_t parts[NS];
 #pragma unroll
-          for (int s = 0; s < NS; ++s) parts[s] = pr[s * pstride + k];
-          acc = parts[0];
+        for (int s = 0; s < NS; ++s) parts[s] = pr[s * pstride + k];
+        f32x4_t acc = parts[0];
 #pragma unroll
-          for (int s = 1; s < NS; ++s) acc += parts[s];
-        } else {  // batches of 8 loads issued before their sums
-          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          for (int s0 = 0; s0 < splits; s0 += 8) {
-            f32x4_t parts[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-              parts[s] = s0 + s < splits ? pr[(s0 + s) * pstride + k] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 8; ++s) acc += parts[s];
-          }
-        }
+        for (int s = 1; s < NS; ++s) acc += parts[s];
         x += acc;
         hr[k] = x;
       }
@@ -141,6 +127,74 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k = threadIdx.x + i * 256;
+    if (k < n4) store_norm4<T>(dst + 4 * k, v[i], inv, g + 4 * k);
+  }
+}
+
+// The same for more than 8 split-K partials (small M, where the GEMM splits
+// K 16-32 ways): four groups of 256 threads each sum every fourth partial of
+// the whole row (loads in batches of 8), the group sums meet in LDS in fixed
+// order, and group 0 finishes the row as above.  A single group would make
+// ~12 dependent memory round trips per row.
+template <class T>
+__global__ __launch_bounds__(1024) void resid_norm_many_kernel(const float* __restrict__ partial, int splits, int M,
+                                                               int H, float* __restrict__ h, const T* __restrict__ g,
+                                                               float eps, T* __restrict__ out, int final_L) {
+  __shared__ f32x4_t sums[3][1024];
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  int orow = r;
+  if (final_L > 0) {
+    const int l = r % final_L;
+    if (l == 0) return;
+    orow = (r / final_L) * (final_L - 1) + l - 1;
+  }
+  const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
+  f32x4_t* hr = (f32x4_t*)(h + (size_t)r * H);
+  const int n4 = H / 4;
+  const size_t pstride = (size_t)M * H / 4;
+  const f32x4_t* pr = (const f32x4_t*)partial + (size_t)r * n4;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = t + i * 256;
+    acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (k >= n4) continue;
+    for (int s0 = grp; s0 < splits; s0 += 32) {  // splits s0, s0 + 4, ..., s0 + 28
+      f32x4_t parts[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        parts[j] = s0 + 4 * j < splits ? pr[(size_t)(s0 + 4 * j) * pstride + k] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i] += parts[j];
+    }
+    if (grp > 0) sums[grp - 1][k] = acc[i];
+  }
+  __syncthreads();
+  f32x4_t v[4];
+  float ss = 0.f;
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = t + i * 256;
+      if (k >= n4) continue;
+      f32x4_t x = hr[k];
+      x += ((acc[i] + sums[0][k]) + sums[1][k]) + sums[2][k];
+      hr[k] = x;
+      v[i] = x;
+      ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (grp != 0) return;
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  T* dst = out + (size_t)orow * H;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = t + i * 256;
     if (k < n4) store_norm4<T>(dst + 4 * k, v[i], inv, g + 4 * k);
   }
 }
@@ -253,7 +307,11 @@ hipError_t residual_norm(int dt, const float* partial, int splits, int M, int H,
       case 6: launch(tag, std::integral_constant<int, 6>{}); break;
       case 7: launch(tag, std::integral_constant<int, 7>{}); break;
       case 8: launch(tag, std::integral_constant<int, 8>{}); break;
-      default: launch(tag, std::integral_constant<int, 0>{});
+      default: {
+        typedef decltype(tag) T;
+        hipLaunchKernelGGL(resid_norm_many_kernel<T>, dim3(grid), dim3(1024), 0, st, partial, splits, M, H, h,
+                           (const T*)g, eps, (T*)out, final_L);
+      }
     }
   };
   if (dt == FPD_DTYPE_BF16)
