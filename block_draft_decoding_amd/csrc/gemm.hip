@@ -723,9 +723,11 @@ GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int sp
   return p;
 }
 
-// Tile and split choice, from measured sweeps on MI355X (block rows M = 16,
-// 25 and 385 of the 2560-wide drafter, weights streamed from HBM, splits
-// 1..8): small M streams the weights with many split-K workgroups; larger M
+// Tile and split choice, from measured sweeps on MI355X (block rows M = 8,
+// 16, 25 and 385 of the 2560-wide drafter, weights streamed from HBM,
+// splits 1..32, split-K sums included; M = 40 and 64 checked): M <= 64
+// splits K until about one pass of workgroups over the 256 CUs (more splits
+// cost more in partial sums than they gain in streaming); larger M
 // takes the 128x256 eight-wave tile (one workgroup per CU) when it alone
 // nearly fills 256 CUs; deep-K or paired outputs split that tile along K so
 // that the row tiles (a partly filled last one counts its share of 32-row
@@ -740,8 +742,8 @@ GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
     while (tiles * s2 < lo && s2 * 2 <= 32 && kt / (s2 * 2) >= 2 && tiles * s2 * 2 <= hi) s2 *= 2;
     return make_plan(cfg, M, ncols, K, nw, paired, s2);
   };
-  if (M <= 32) return with_splits(GEMM_32x128_S4, 1024, 2048);
-  if (M <= 64) return with_splits(GEMM_64x128_S3, 1024, 2048);
+  if (M <= 32) return with_splits(GEMM_32x128_S4, 128, 256);
+  if (M <= 64) return with_splits(GEMM_64x128_S3, 128, 256);
   const GemmPlan big = make_plan(GEMM_128x256_W8_S3, M, ncols, K, nw, paired, 1);
   const GemmPlan folded = make_plan(GEMM_128x256_W8_S3, M, ncols, K, nw, paired, 1, /*fold=*/true);
   // A few leftover rows would otherwise form a second wave of one-row tiles,

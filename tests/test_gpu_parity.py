@@ -254,6 +254,25 @@ def test_full_size_workload(name):
             progress(f"[pairs] off-frame tokens {n_off} of {g.toks.numel()}")
 
 
+def test_full_size_two_trajectory_blocks():
+    """Two 8-waypoint blocks in one call (M = 50 rows, each with its own
+    context): the 64-row GEMM tiles with their split-K sums at the drafter's
+    real widths."""
+    wl = synth.scaled_workload("traj2d", batch=2)
+    inp = synth.make_inputs(wl)
+    g = GpuCase(wl, inp)
+    g.fuse()
+    g.draft()
+    lg = g.argmax(logits=True)
+    torch.cuda.synchronize()
+    progress("[gpu] traj2d x2 done")
+    res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
+    compare_all(wl, g, lg, res, "bf16", "full traj2d x2")
+    k, f = g.validate()
+    ko, fo = O.validate_primitive(g.toks.cpu().numpy(), res["layout"])
+    assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
+
+
 def test_full_size_points3d_sampled():
     """B=8, L=2433, C=4096: the oracle cannot run the whole block in seconds,
     so the sampled checks are: the LM head, argmax and validator on the GPU's
