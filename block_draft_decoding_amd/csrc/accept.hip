@@ -1,6 +1,8 @@
 // Block acceptance: the schema validator for primitives (VFlash paper §2.5)
 // and greedy longest-prefix verification for text (VFlash paper §2.1; blog
-// "Method").  One wavefront per batch row; decisions are exact integer work.
+// "Method").  The validator (and box acceptance) runs one workgroup per
+// request, verification one wavefront per row; decisions are exact integer
+// work.
 #include <climits>
 
 #include "../../include/fpd.h"

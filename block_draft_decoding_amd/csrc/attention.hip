@@ -5,8 +5,9 @@
 // bf16 path (gfx950 MFMA 32x32x16): the n_q/n_kv query heads that share a
 // KV head are packed into one M dimension (rows r = head_in_group * L + l,
 // contiguous in the [B, n_q, L, d] query layout).  Each wave owns 32 packed
-// query rows; a workgroup of 4 waves shares 64-key K / V^T tiles staged in
-// LDS with a register prefetch of the next tile.  Scores are computed
+// query rows; a workgroup of 8 waves (256 rows) shares 64-key K / V^T tiles
+// that stream global -> LDS through a 3-stage ring of LDS-writing buffer
+// loads (two tiles in flight, one barrier per tile).  Scores are computed
 // transposed, S^T = K Q^T, so every lane owns one query: the online softmax
 // needs a single cross-lane exchange (lane l with lane l ^ 32).  K rows are
 // read with bits 2 and 3 of the row index swapped, which makes the S^T

@@ -1,10 +1,11 @@
 // Dense projections of the drafter: Y = A W^T with fused epilogues.
 //
-// bf16 path: MFMA 32x32x16 (gfx950) tiles, A and W both K-contiguous, staged
-// through LDS with a register prefetch of the next K-tile (one barrier per
-// K-tile), split-K with a fixed-order reduction when the tile count alone
-// cannot fill 256 CUs, and an XCD-aware tile order so the workgroups that
-// share a weight tile run on the same XCD.
+// bf16 path: MFMA 32x32x16 (gfx950) tiles, A and W both K-contiguous,
+// streamed global -> LDS through a 2-4 stage ring of LDS-writing buffer loads
+// (one barrier per K-tile), split-K with a fixed-order reduction when the
+// tile count alone cannot fill 256 CUs, an XCD-aware tile order so the
+// workgroups that share a weight tile run on the same XCD, and a last row
+// tile that can carry up to 16 leftover rows.
 //
 // "Paired" epilogues need two W rows per output (RoPE rotates column i with
 // column i + d/2 of a head; SwiGLU combines gate row i with up row I + i).

@@ -1,4 +1,4 @@
-// Device helpers of the global -> LDS pipelines (GEMM, constrained LM head):
+// Device helpers of the global -> LDS pipelines (GEMM, attention, LM head):
 // LDS-writing buffer loads, the bank swizzle of 16-byte chunks, fence-free
 // workgroup barriers and explicit memory-counter waits.
 #pragma once
