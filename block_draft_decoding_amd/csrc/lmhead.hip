@@ -20,7 +20,12 @@ constexpr int BK = 64;
 constexpr int HBM = 32;    // rows per tile (bf16)
 constexpr int HBN = 128;   // columns per chunk (bf16): 4 waves x 32
 constexpr int HBN_NARROW = 32;  // one wave: for layouts whose 128-column chunks give few work items
-constexpr int HST = 4;     // depth of the global -> LDS ring (bf16)
+// depth of the global -> LDS ring (bf16): 3 for the wide chunks, so that two
+// workgroups fit in a CU's 160 KB of LDS (4 stages come to just over 80 KB
+// with the reduction arrays: 183 -> 148 us for a full-vocabulary text block,
+// measured); 4 for the narrow ones (32 KB)
+constexpr int HST_WIDE = 3;
+constexpr int HST_NARROW = 4;
 constexpr int FBM = 16;    // f32 path: rows per tile
 constexpr int FBN = 64;    // f32 path: columns per chunk
 
@@ -60,7 +65,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& c, int width) {
 // buffer loads (K-tile offsets are scalar; each lane's row offset is fixed),
 // so several K-tiles are in flight while the MFMAs run.  16-byte chunks are
 // bank-swizzled as in the dense GEMM.  One wave per 32 columns of the chunk.
-template <int CN>
+template <int CN, int HST>
 __global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
   constexpr int HW = CN / 32;                      // waves
   constexpr int NT = 64 * HW;
@@ -343,9 +348,10 @@ hipError_t lm_head_partials(int dt, const HeadArgs& a, hipStream_t st) {
   for (int s = 0; s < a.n_sets; ++s)
     if ((size_t)a.sets[s].n_cols * a.H * 2 > 0xffffffffull) return hipErrorInvalidValue;
   if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN_NARROW)
-    hipLaunchKernelGGL(head_bf16_kernel<HBN_NARROW>, dim3((unsigned)items), dim3(2 * HBN_NARROW), 0, st, a);
+    hipLaunchKernelGGL((head_bf16_kernel<HBN_NARROW, HST_NARROW>), dim3((unsigned)items), dim3(2 * HBN_NARROW), 0, st,
+                       a);
   else if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN)
-    hipLaunchKernelGGL(head_bf16_kernel<HBN>, dim3((unsigned)items), dim3(2 * HBN), 0, st, a);
+    hipLaunchKernelGGL((head_bf16_kernel<HBN, HST_WIDE>), dim3((unsigned)items), dim3(2 * HBN), 0, st, a);
   else if (dt == FPD_DTYPE_BF16)
     return hipErrorInvalidValue;
   else
