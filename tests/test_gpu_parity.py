@@ -86,6 +86,17 @@ def test_small_bf16_end_to_end(kind, B, C, over):
         progress(f"[pairs] off-frame tokens {n_off} of {res['tokens'].size}")
 
 
+def test_more_than_eight_split_partials():
+    """A narrow drafter with a wide MLP (hidden 512, MLP 4096): at 16 block
+    rows the down projection splits K 32 ways (one pass of workgroups over
+    the CUs), so its split-K sums take the four-group residual + RMSNorm
+    kernel."""
+    shape = replace(SMALL, inter=4096)
+    wl = small_workload("text", 1, 64, seed=73, shape=shape, block_len=16)
+    inp, g, lg, res = run_both(wl)
+    compare_all(wl, g, lg, res, "bf16", "16-way split-K sums")
+
+
 @pytest.mark.parametrize("n_layers", [1, 2, 3])
 def test_per_layer_hidden_parity(n_layers):
     shape = replace(SMALL, n_layers=3)
