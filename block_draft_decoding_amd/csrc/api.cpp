@@ -32,6 +32,11 @@ int32_t fail(int32_t code, const std::string& msg) {
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 int round8(int x) { return (x + 7) & ~7; }
 
+// Row counts (B x positions) are kept in int arithmetic by the launches;
+// beyond 2^24 rows the workspace alone would exceed any GPU's memory.
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+bool too_many_rows(int32_t B, int32_t n) { return (int64_t)B * n > kMaxRows; }
+
 }  // namespace
 
 struct fpd_drafter {
@@ -342,6 +347,7 @@ int32_t fpd_layout_masks(const fpd_layout* lay, fpd_layout_sizes* sizes, int32_t
 int32_t fpd_workspace_size(const fpd_drafter* d, int32_t B, int32_t C, int32_t L, size_t* bytes) {
   if (!d || !bytes) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || C < 0 || L < 2) return fail(FPD_E_SHAPE, "need B >= 1, C >= 0, L >= 2");
+  if (too_many_rows(B, C) || too_many_rows(B, L)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   // LM-head partials: wide chunks of the whole vocabulary, or narrow chunks,
   // which are used only while the wide ones number under 128 per launch
   // (at most 4 x 127 narrow chunks in a row)
@@ -401,6 +407,7 @@ int32_t fpd_fuse_context_kv(const fpd_drafter* d, const void* feats, int32_t B, 
                             void* stream) {
   if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || C < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C >= 1, pos0 >= 0");
+  if (too_many_rows(B, C)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   if (ctx_cap < C || ctx_cap % 8) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
   return fuse_rows(d, feats, B, C, pos0, (char*)ctx_k, (char*)ctx_v, ctx_cap, ws, ws_bytes, stream);
 }
@@ -410,6 +417,7 @@ int32_t fpd_append_context_kv(const fpd_drafter* d, const void* feats, int32_t B
                               void* stream) {
   if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || C_new < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C_new >= 1, pos0 >= 0");
+  if (too_many_rows(B, C_new)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   if (ctx_cap % 8 || (int64_t)pos0 + C_new > ctx_cap)
     return fail(FPD_E_SHAPE, "ctx_cap must be a multiple of 8 and hold pos0 + C_new keys");
   // key row pos0 of every (layer, b, kv head) segment: the K rows are d
@@ -428,6 +436,7 @@ int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32
                    size_t ws_bytes, void* stream, bool shared_ctx) {
   if (!d || !tokens || !hidden_out) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || L < 2 || C < 0 || block_pos < 0) return fail(FPD_E_SHAPE, "need B >= 1, L >= 2, C >= 0, block_pos >= 0");
+  if (too_many_rows(B, L) || too_many_rows(B, C)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   if (C > 0 && (!ctx_k || !ctx_v)) return fail(FPD_E_ARG, "null context");
   if (C > 0 && (ctx_cap < C || ctx_cap % 8)) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
   const DraftWs w = plan_draft(*d, B, L, C);
@@ -493,6 +502,7 @@ int32_t fpd_constrained_argmax(const fpd_drafter* d, const fpd_layout* lay, cons
   if (!d || !lay || !hidden || !tokens_out) return fail(FPD_E_ARG, "null argument");
   if (lay->d != d) return fail(FPD_E_ARG, "layout was created for another drafter");
   if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+  if (too_many_rows(B, lay->host.L)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   const HostLayout& h = lay->host;
   const fpd_config& c = d->cfg;
   const int L = h.L, ns = h.n_sets();
@@ -561,6 +571,7 @@ int32_t fpd_validate_primitive(const fpd_layout* lay, const int32_t* tokens, int
                                int32_t* first_invalid_out, void* stream) {
   if (!lay || !tokens || !k_out || !first_invalid_out) return fail(FPD_E_ARG, "null argument");
   if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+  if (too_many_rows(B, lay->host.L)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   FPD_TRY_HIP(validate_primitive(validate_args(lay, tokens, B, k_out, first_invalid_out), (hipStream_t)stream));
   return FPD_OK;
 }
@@ -571,6 +582,7 @@ int32_t fpd_accept_boxes(const fpd_layout* lay, const int32_t* tokens, const flo
     return fail(FPD_E_ARG, "null argument");
   if (std::isnan(tau)) return fail(FPD_E_ARG, "tau is NaN");
   if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
+  if (too_many_rows(B, lay->host.L)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   ValidateArgs a = validate_args(lay, tokens, B, k_out, first_invalid_out);
   a.conf = conf, a.coord = lay->coord, a.tau = tau, a.uncertain_out = first_uncertain_out;
   FPD_TRY_HIP(validate_primitive(a, (hipStream_t)stream));
@@ -581,6 +593,7 @@ int32_t fpd_verify_prefix(const int32_t* draft, const int32_t* target, int32_t B
                           int32_t* next_out, void* stream) {
   if (!draft || !target || !k_out || !next_out) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || L < 2) return fail(FPD_E_SHAPE, "need B >= 1 and L >= 2");
+  if (too_many_rows(B, L)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
   FPD_TRY_HIP(verify_prefix(draft, target, B, L, k_out, next_out, (hipStream_t)stream));
   return FPD_OK;
 }

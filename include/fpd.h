@@ -58,7 +58,8 @@ extern "C" {
 enum {
   FPD_OK = 0,
   FPD_E_ARG = 1,          /* null pointer, bad enum, negative size           */
-  FPD_E_SHAPE = 2,        /* inconsistent sizes between arguments            */
+  FPD_E_SHAPE = 2,        /* inconsistent sizes between arguments, or more   */
+                          /* than 2^24 rows (B x positions) in one call      */
   FPD_E_DTYPE = 3,        /* unknown dtype                                    */
   FPD_E_SCHEMA = 4,       /* schema expands to an invalid layout              */
   FPD_E_WORKSPACE = 5,    /* workspace smaller than fpd_workspace_size()      */

@@ -135,6 +135,9 @@ def test_hot_calls_reject_bad_arguments_without_gpu_work():
         n = ctypes.c_size_t()
         assert fpd._ws_size(h, 1, 64, 16, ctypes.byref(n)) == fpd.FPD_OK and n.value > 0
         assert fpd._ws_size(h, 0, 64, 16, ctypes.byref(n)) == fpd.FPD_E_SHAPE
+        # more than 2^24 rows
+        assert fpd._ws_size(h, 1 << 12, 1 << 13, 16, ctypes.byref(n)) == fpd.FPD_E_SHAPE
+        assert fpd._verify(8, 8, 1 << 20, 17, 8, 8, None) == fpd.FPD_E_SHAPE
         # null tokens / outputs
         assert fpd._draft(h, None, 1, 16, None, None, 0, 0, 0, None, None, 0, None) == fpd.FPD_E_ARG
         # L < 2
