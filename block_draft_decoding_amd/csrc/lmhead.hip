@@ -23,9 +23,18 @@ constexpr int HBN_NARROW = 32;  // one wave: for layouts whose 128-column chunks
 // depth of the global -> LDS ring (bf16): 3 for the wide chunks, so that two
 // workgroups fit in a CU's 160 KB of LDS (4 stages come to just over 80 KB
 // with the reduction arrays: 183 -> 148 us for a full-vocabulary text block,
-// measured); 4 for the narrow ones (32 KB)
+// measured); 4 for the narrow ones (32 KB per K group; four K groups come
+// to 140 KB, one workgroup per CU)
 constexpr int HST_WIDE = 3;
 constexpr int HST_NARROW = 4;
+constexpr int kCUs = 256;
+// K groups of a narrow-chunk item: the most (4, 2 or 1) that divide the K
+// tiles and keep K groups x items within one per CU
+int head_k_groups(int items, int H) {
+  for (int kw = 4; kw > 1; kw /= 2)
+    if ((long)items * kw <= kCUs && H % (BK * kw) == 0) return kw;
+  return 1;
+}
 constexpr int FBM = 16;    // f32 path: rows per tile
 constexpr int FBN = 64;    // f32 path: columns per chunk
 
@@ -64,11 +73,15 @@ __device__ __forceinline__ void wave_argmax(float& v, int& c, int width) {
 // W_lm rows stream global -> LDS through an HST-deep ring of LDS-writing
 // buffer loads (K-tile offsets are scalar; each lane's row offset is fixed),
 // so several K-tiles are in flight while the MFMAs run.  16-byte chunks are
-// bank-swizzled as in the dense GEMM.  One wave per 32 columns of the chunk.
-template <int CN, int HST>
-__global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
-  constexpr int HW = CN / 32;                      // waves
-  constexpr int NT = 64 * HW;
+// bank-swizzled as in the dense GEMM.  One wave per 32 columns of the chunk;
+// with KW > 1, KW such groups of waves each take 1/KW of the K range through
+// a ring of their own, and their partial tiles are summed in LDS in group
+// order before the epilogue (a chunk's single wave would otherwise stream
+// the item's whole 330 KB alone).
+template <int CN, int HST, int KW>
+__global__ __launch_bounds__(2 * CN * KW) void head_bf16_kernel(HeadArgs a) {
+  constexpr int HW = CN / 32;                      // column waves of a K group
+  constexpr int NT = 64 * HW;                      // threads of a K group
   constexpr int CH = BK / 8;                       // 16-byte chunks per tile row
   constexpr int STAGE = (HBM + CN) * CH;           // chunks per stage
   constexpr int AI = HBM * CH / NT;                // A loads per thread and stage
@@ -76,12 +89,13 @@ __global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
   constexpr int LPS = AI + BI;
   static_assert(AI * NT == HBM * CH && BI * NT == CN * CH, "tile shape");
   static_assert(LPS * (HST - 1) < 64, "pipeline depth");
-  __shared__ u32x4_t lds[HST * STAGE];
+  __shared__ u32x4_t lds[KW * HST * STAGE];
   __shared__ float red_v[HW][HBM];
   __shared__ int red_c[HW][HBM];
   __shared__ int rowmap[HBM];  // hidden / output row of each tile row (rows past the set repeat a valid one)
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gwave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = gwave / HW, wave = gwave % HW;    // K group, column wave within it
   const int lq = lane & 31, lg = lane >> 5;
   const Item it = find_item(a, xcd_remap(blockIdx.x, gridDim.x), HBM);
   if (it.set < 0) return;
@@ -107,9 +121,10 @@ __global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
     const int col = min(c0 + r, S.n_cols - 1);
     boff[i] = (uint32_t)(((size_t)col * H + c * 8) * 2);
   }
+  u32x4_t* ring = lds + kw * HST * STAGE;
   auto issue = [&](int kt, int stage) {
     const int soff = kt * BK * 2;
-    u32x4_t* base = lds + stage * STAGE;
+    u32x4_t* base = ring + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < AI; ++i) lds_dma16(arsrc, base + (wave * AI + i) * 64, aoff[i], soff);
 #pragma unroll
@@ -119,13 +134,13 @@ __global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int KT = H / BK;
+  const int KT = H / BK / KW, kt0 = kw * KT;       // this group's K tiles (KW divides H / BK)
 #pragma unroll
   for (int s = 0; s < HST; ++s)
-    if (s < KT) issue(s, s);
+    if (s < KT) issue(kt0 + s, s);
   bf16x8_t af[2], bfv[2];
   auto fetch = [&](int stage, int kk, int buf) {
-    const u32x4_t* As = lds + stage * STAGE;
+    const u32x4_t* As = ring + stage * STAGE;
     af[buf] = __builtin_bit_cast(bf16x8_t, As[swz<CH>(lq, kk * 2 + lg)]);
     bfv[buf] = __builtin_bit_cast(bf16x8_t, As[HBM * CH + swz<CH>(wave * 32 + lq, kk * 2 + lg)]);
   };
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
         wait_lgkm0();
         if (kt + 1 < KT) wait_stages<LPS, HST - 2>(min(HST - 2, KT - 2 - kt));
         barrier_nofence();
-        if (kt + HST < KT) issue(kt + HST, stage);
+        if (kt + HST < KT) issue(kt0 + kt + HST, stage);
         if (kt + 1 < KT) fetch((kt + 1) % HST, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -152,6 +167,17 @@ __global__ __launch_bounds__(2 * CN) void head_bf16_kernel(HeadArgs a) {
     }
   }
 
+  if constexpr (KW > 1) {  // sum the groups' partial tiles in group order
+    __shared__ f32x16_t kpart[KW - 1][HW][64];
+    if (kw > 0) kpart[kw - 1][wave][lane] = acc;
+    __syncthreads();
+    if (kw > 0) {
+      __syncthreads();  // the epilogue's barrier below
+      return;
+    }
+#pragma unroll
+    for (int g2 = 0; g2 < KW - 1; ++g2) acc += kpart[g2][wave][lane];
+  }
   // epilogue: this lane holds column n of rows rr(r)
   const int n = c0 + wave * 32 + lq;
   const bool ncol = n < S.n_cols;
@@ -347,11 +373,21 @@ hipError_t lm_head_partials(int dt, const HeadArgs& a, hipStream_t st) {
   if ((size_t)a.B * (a.L - 1) * a.H * 2 > 0xffffffffull) return hipErrorInvalidValue;
   for (int s = 0; s < a.n_sets; ++s)
     if ((size_t)a.sets[s].n_cols * a.H * 2 > 0xffffffffull) return hipErrorInvalidValue;
-  if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN_NARROW)
-    hipLaunchKernelGGL((head_bf16_kernel<HBN_NARROW, HST_NARROW>), dim3((unsigned)items), dim3(2 * HBN_NARROW), 0, st,
-                       a);
-  else if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN)
-    hipLaunchKernelGGL((head_bf16_kernel<HBN, HST_WIDE>), dim3((unsigned)items), dim3(2 * HBN), 0, st, a);
+  if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN_NARROW) {
+    // split K within the item while the items, so multiplied, still fit in
+    // one workgroup per CU (a second pass of workgroups costs more)
+    const int kw = head_k_groups(items, a.H);
+    if (kw == 4)
+      hipLaunchKernelGGL((head_bf16_kernel<HBN_NARROW, HST_NARROW, 4>), dim3((unsigned)items), dim3(2 * HBN_NARROW * 4),
+                         0, st, a);
+    else if (kw == 2)
+      hipLaunchKernelGGL((head_bf16_kernel<HBN_NARROW, HST_NARROW, 2>), dim3((unsigned)items), dim3(2 * HBN_NARROW * 2),
+                         0, st, a);
+    else
+      hipLaunchKernelGGL((head_bf16_kernel<HBN_NARROW, HST_NARROW, 1>), dim3((unsigned)items), dim3(2 * HBN_NARROW), 0,
+                         st, a);
+  } else if (dt == FPD_DTYPE_BF16 && a.chunk_cols == HBN)
+    hipLaunchKernelGGL((head_bf16_kernel<HBN, HST_WIDE, 1>), dim3((unsigned)items), dim3(2 * HBN), 0, st, a);
   else if (dt == FPD_DTYPE_BF16)
     return hipErrorInvalidValue;
   else

@@ -65,9 +65,13 @@ def compare_all(wl, g, lg, res, dtype, name=""):
     return stats
 
 
+# The constrained LM head takes 32-column chunks for all but the text cases;
+# their work items split K four ways (traj2d: 33 items), two ways (traj2d3d,
+# B = 2: 97 items) or not at all (traj2d3d, B = 4: 161 items).
 @pytest.mark.parametrize("kind,B,C,over", [
     ("text", 2, 300, dict(block_len=37)),
     ("traj2d3d", 2, 300, dict(n_points=7, off_id=4099 - 1020 + 1002)),
+    ("traj2d3d", 4, 64, dict(n_points=7, off_id=4099 - 1020 + 1002)),
     ("points3d_text", 3, 77, dict(n_points=2)),
     ("traj2d", 1, 0, dict(n_points=1)),
     ("text", 1, 64, dict(block_len=2)),
