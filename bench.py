@@ -132,6 +132,7 @@ def main():
     dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     w = fpd.weights_to_device(inp.weights, dt)
     d = fpd.fpd_drafter_create(fpd.make_config(s), w)
+    fpd.fpd_drafter_prepare(d)
     lay = fpd.fpd_layout_create(d, wl.schema)
     L, B, C = lay.L, wl.batch, wl.ctx
     cap = (C + 7) // 8 * 8

@@ -45,6 +45,11 @@ struct fpd_drafter {
   std::vector<fpd_layer_weights> layers;
   RopeTab tab;
   int esz;
+  // K-tile-contiguous copies of the projections (fpd_drafter_prepare): one
+  // device buffer; per layer q/k/v, O, gate/up and down, then the fusion map
+  void* tiled = nullptr;
+  std::vector<const void*> t_qkv, t_o, t_gu, t_d;
+  const void* t_fc = nullptr;
 };
 
 struct fpd_layout {
@@ -220,7 +225,42 @@ int32_t fpd_drafter_create(const fpd_config* cfg, const fpd_weights* w, fpd_draf
 }
 
 int32_t fpd_drafter_destroy(fpd_drafter* d) {
+  if (d && d->tiled) (void)hipFree(d->tiled);
   delete d;
+  return FPD_OK;
+}
+
+int32_t fpd_drafter_prepare(fpd_drafter* d, void* stream) {
+  if (!d) return fail(FPD_E_ARG, "null drafter");
+  const fpd_config& c = d->cfg;
+  if (c.dtype != FPD_DTYPE_BF16 || d->tiled) return FPD_OK;
+  const int H = c.hidden, dh = c.head_dim, qd = c.n_q * dh, nqkv = (c.n_q + 2 * c.n_kv) * dh;
+  const size_t e_qkv = gemm_tiles_elems(nqkv, H), e_o = gemm_tiles_elems(H, qd),
+               e_gu = gemm_tiles_elems(2 * c.inter, H), e_d = gemm_tiles_elems(H, c.inter),
+               e_fc = gemm_tiles_elems(H, c.n_fused * H);
+  const size_t per_layer = e_qkv + e_o + e_gu + e_d;
+  void* buf = nullptr;
+  hipError_t e = hipMalloc(&buf, (per_layer * c.n_layers + e_fc) * 2);
+  if (e != hipSuccess) return fail(FPD_E_HIP, std::string("tiled weights: ") + hipGetErrorString(e));
+  hipStream_t s = (hipStream_t)stream;
+  bf16_t* p = (bf16_t*)buf;
+  std::vector<const void*> tq, to, tg, td;
+  for (int li = 0; li < c.n_layers && e == hipSuccess; ++li) {
+    const fpd_layer_weights& lw = d->layers[li];
+    tq.push_back(p), e = gemm_pack_tiles(lw.w_qkv, nqkv, H, p, s), p += e_qkv;
+    if (e == hipSuccess) to.push_back(p), e = gemm_pack_tiles(lw.w_o, H, qd, p, s), p += e_o;
+    if (e == hipSuccess) tg.push_back(p), e = gemm_pack_tiles(lw.w_gu, 2 * c.inter, H, p, s), p += e_gu;
+    if (e == hipSuccess) td.push_back(p), e = gemm_pack_tiles(lw.w_d, H, c.inter, p, s), p += e_d;
+  }
+  const void* tfc = p;
+  if (e == hipSuccess) e = gemm_pack_tiles(d->w.w_fc, H, c.n_fused * H, p, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(buf);
+    return fail(FPD_E_HIP, std::string("tiled weights: ") + hipGetErrorString(e));
+  }
+  d->tiled = buf;
+  d->t_qkv = tq, d->t_o = to, d->t_gu = tg, d->t_d = td, d->t_fc = tfc;
   return FPD_OK;
 }
 
@@ -381,7 +421,7 @@ int32_t fuse_rows(const fpd_drafter* d, const void* feats, int32_t B, int32_t C,
   }
   float* Z = (float*)wsp(ws, w.z);
   float* part = (float*)wsp(ws, w.partial);
-  FPD_TRY_HIP(gemm_store_f32(dt, X, c.n_fused * H, M, c.n_fused * H, d->w.w_fc, H, Z, H, part,
+  FPD_TRY_HIP(gemm_store_f32(dt, X, c.n_fused * H, M, c.n_fused * H, Wt{d->w.w_fc, d->t_fc}, H, Z, H, part,
                              w.partial_bytes, s, "gemm_fc"));
   void* Zn = wsp(ws, w.zn);
   FPD_TRY_HIP(rmsnorm_rows(dt, Z, H, M, M, 0, 0, d->w.g_fc, c.rms_eps, Zn, s));
@@ -393,7 +433,9 @@ int32_t fuse_rows(const fpd_drafter* d, const void* feats, int32_t B, int32_t C,
     o.C = C, o.cap = ctx_cap, o.nkv = c.n_kv, o.d = dh, o.pos0 = rope_pos0, o.rope = c.use_rope;
     o.tab = d->tab;
     const char* wkv = (const char*)d->layers[li].w_qkv + (size_t)c.n_q * dh * H * d->esz;
-    FPD_TRY_HIP(gemm_ctx_kv(dt, Zn, M, H, wkv, o, part, w.partial_bytes, s));
+    // the K/V rows start at row n_q * d, a whole 32-row group of the tiled copy
+    const void* tkv = d->tiled ? (const char*)d->t_qkv[li] + (size_t)c.n_q * dh * H * d->esz : nullptr;
+    FPD_TRY_HIP(gemm_ctx_kv(dt, Zn, M, H, Wt{wkv, tkv}, o, part, w.partial_bytes, s));
   }
   return FPD_OK;
 }
@@ -456,7 +498,8 @@ int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32
     qo.q = wsp(ws, w.q), qo.k = wsp(ws, w.kb), qo.vt = wsp(ws, w.vbt);
     qo.L = L, qo.Lp = round8(L), qo.nq = c.n_q, qo.nkv = c.n_kv, qo.d = dh, qo.pos0 = block_pos;
     qo.rope = c.use_rope, qo.tab = d->tab;
-    FPD_TRY_HIP(gemm_qkv(dt, a, M, H, lw.w_qkv, qo, part, w.partial_bytes, s));
+    const bool tl = d->tiled != nullptr;
+    FPD_TRY_HIP(gemm_qkv(dt, a, M, H, Wt{lw.w_qkv, tl ? d->t_qkv[li] : nullptr}, qo, part, w.partial_bytes, s));
     AttnArgs at{};
     at.q = qo.q, at.kb = qo.k, at.vbt = qo.vt;
     at.ck = C > 0 ? (const char*)ctx_k + li * ctx_layer : nullptr;
@@ -467,13 +510,16 @@ int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32
     at.scale = (float)(1.0 / std::sqrt((double)dh));
     FPD_TRY_HIP(attention(dt, at, wsp(ws, w.attn), w.attn_bytes, s));
     // h += O W_o^T, a = RMSNorm(h) for the MLP
-    FPD_TRY_HIP(gemm_residual_norm(dt, at.o, M, qd, lw.w_o, H, h, lw.g_mlp, c.rms_eps, a, 0, part, w.partial_bytes, s,
+    FPD_TRY_HIP(gemm_residual_norm(dt, at.o, M, qd, Wt{lw.w_o, tl ? d->t_o[li] : nullptr}, H, h, lw.g_mlp, c.rms_eps,
+                                   a, 0, part, w.partial_bytes, s,
                                    "gemm_o"));
     void* u = wsp(ws, w.u);
-    FPD_TRY_HIP(gemm_swiglu(dt, a, M, H, lw.w_gu, c.inter, u, part, w.partial_bytes, s));
+    FPD_TRY_HIP(gemm_swiglu(dt, a, M, H, Wt{lw.w_gu, tl ? d->t_gu[li] : nullptr}, c.inter, u, part, w.partial_bytes,
+                            s));
     // h += u W_d^T, then the next layer's attention norm, or the final norm over positions 1..L-1
     const bool last = li + 1 == c.n_layers;
-    FPD_TRY_HIP(gemm_residual_norm(dt, u, M, c.inter, lw.w_d, H, h, last ? d->w.g_final : d->layers[li + 1].g_attn,
+    FPD_TRY_HIP(gemm_residual_norm(dt, u, M, c.inter, Wt{lw.w_d, tl ? d->t_d[li] : nullptr}, H, h,
+                                   last ? d->w.g_final : d->layers[li + 1].g_attn,
                                    c.rms_eps, last ? hidden_out : a, last ? L : 0, part, w.partial_bytes, s,
                                    "gemm_down"));
   }

@@ -53,24 +53,40 @@ int gemm_cfg_extra_rows(int cfg, bool paired);
 // nw = W rows covered (partial row length), paired = two W rows per column.
 GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired);
 
+// ---- K-tile-contiguous copies of the weights ----------------------------------
+// A projection's weights: row-major W [rows, K] (torch Linear layout) and,
+// once the drafter is prepared, the same matrix with each 32-row group's
+// 64-deep K-tiles stored one after another (element (r, k) at
+// ((r / 32 * K / 64 + k / 64) * 32 + r % 32) * 64 + k % 64), so a
+// workgroup's weight tile for one K step is 4 KB-contiguous runs instead of
+// 128-byte pieces of rows 2 K bytes apart (nullptr before).
+struct Wt {
+  const void* w;
+  const void* tiled;
+};
+// Elements (bf16) of the tiled copy of a [rows, K] matrix (rows rounded up to 32).
+size_t gemm_tiles_elems(int rows, int K);
+// Writes that copy (rows past the matrix are zero).  K must be a multiple of 64.
+hipError_t gemm_pack_tiles(const void* W, int rows, int K, void* Wtiled, hipStream_t st);
+
 // ---- Y = A W^T with epilogues --------------------------------------------
 // A [M, K] row-major (lda), W [.., K] row-major (ldw = K).  dt: FPD_DTYPE_*.
 // `partial`/`partial_bytes`: split-K scratch from the workspace.
 
 // out[m, n] = Y (float).  N outputs.
-hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const void* W, int N,
+hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const Wt& W, int N,
                           float* out, int ldo, float* partial, size_t partial_bytes, hipStream_t st,
                           const char* tag);
 
 // h[m, n] += Y (float residual).
-hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const void* W, int N,
+hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const Wt& W, int N,
                          float* h, int ldh, float* partial, size_t partial_bytes, hipStream_t st,
                          const char* tag);
 
 // h += A W^T, then out = RMSNorm(h) * g (bf16 split-K partials are summed in
 // the fused row-wise norm kernel).  final_L > 0: output only rows with
 // l = r % final_L >= 1, at b*(L-1) + l - 1.
-hipError_t gemm_residual_norm(int dt, const void* A, int M, int K, const void* W, int H, float* h, const void* g,
+hipError_t gemm_residual_norm(int dt, const void* A, int M, int K, const Wt& W, int H, float* h, const void* g,
                               float eps, void* out, int final_L, float* partial, size_t partial_bytes,
                               hipStream_t st, const char* tag);
 
@@ -81,7 +97,7 @@ struct QkvOut {
   int L, Lp, nq, nkv, d, pos0, rope;
   RopeTab tab;
 };
-hipError_t gemm_qkv(int dt, const void* A, int M, int K, const void* Wqkv, const QkvOut& o,
+hipError_t gemm_qkv(int dt, const void* A, int M, int K, const Wt& Wqkv, const QkvOut& o,
                     float* partial, size_t partial_bytes, hipStream_t st);
 
 // Context K/V of one drafter layer from the fused features, rows m = b * C + c:
@@ -91,11 +107,11 @@ struct CtxOut {
   int C, cap, nkv, d, pos0, rope;
   RopeTab tab;
 };
-hipError_t gemm_ctx_kv(int dt, const void* Zn, int M, int K, const void* Wkv, const CtxOut& o,
+hipError_t gemm_ctx_kv(int dt, const void* Zn, int M, int K, const Wt& Wkv, const CtxOut& o,
                        float* partial, size_t partial_bytes, hipStream_t st);
 
 // u[m, i] = silu(A Wg^T)[m, i] * (A Wu^T)[m, i], W = [gate rows; up rows] ([2I, K]).
-hipError_t gemm_swiglu(int dt, const void* A, int M, int K, const void* Wgu, int I, void* u,
+hipError_t gemm_swiglu(int dt, const void* A, int M, int K, const Wt& Wgu, int I, void* u,
                        float* partial, size_t partial_bytes, hipStream_t st);
 
 }  // namespace fpd

@@ -146,8 +146,8 @@ __device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, i
 // weight column once more from HBM for r rows of work.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int XR, bool PAIRED, class Map, class Epi>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, int w_rows, Map map,
-    int ncols, Epi epi, float* __restrict__ partial, int part_ld, int m_tiles, int n_tiles,
+    const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, int w_rows, int w_tiled,
+    Map map, int ncols, Epi epi, float* __restrict__ partial, int part_ld, int m_tiles, int n_tiles,
     int splits) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int NT = 64 * NW;
@@ -192,8 +192,10 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   // forces a full LDS wait before every MFMA group).
   const __amdgpu_buffer_rsrc_t arsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)((size_t)M * lda * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t brsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)((size_t)w_rows * K * 2), 0x00020000);
+  // W row-major, or K-tile-contiguous (w_tiled: each 32-row group's 64-deep
+  // K-tiles one after another, rows padded to 32)
+  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)W, (short)0, (int)((size_t)(w_tiled ? (w_rows + 31) / 32 * 32 : w_rows) * K * 2), 0x00020000);
   uint32_t aoff[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
@@ -212,7 +214,8 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     } else {
       wrow = map.row(min(c0 + r, ncols - 1));
     }
-    boff[i] = (uint32_t)(((size_t)wrow * K + c * 8) * 2);
+    boff[i] = w_tiled ? (uint32_t)((((size_t)(wrow / 32) * (K / 64) * 32 + wrow % 32) * 64 + c * 8) * 2)
+                      : (uint32_t)(((size_t)wrow * K + c * 8) * 2);
   }
   // extra rows: instruction i of a wave fills 16 slots (256 bytes); lane
   // `lane` writes word lane % 4 of slot lane / 4
@@ -226,11 +229,12 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   }
   auto issue = [&](int kt, int stage, auto ext_c) {
     const int soff = kt * BK * 2;
+    const int k0 = kt * BK, sb = w_tiled ? (k0 / 64) * 4096 + (k0 % 64) * 2 : soff;
     u32x4_t* base = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < AI; ++i) lds_dma16(arsrc, base + (wave * AI + i) * 64, aoff[i], soff);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + AR * CH + (wave * BI + i) * 64, boff[i], soff);
+    for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + AR * CH + (wave * BI + i) * 64, boff[i], sb);
     if constexpr (decltype(ext_c)::value) {
 #pragma unroll
       for (int i = 0; i < XI; ++i) lds_dma4(arsrc, base + BM * CH + (wave * XI + i) * 16, xoff[i], soff);
@@ -439,6 +443,22 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   }
 }
 
+// K-tile-contiguous copy (see Wt): one thread per 16-byte piece.
+__global__ __launch_bounds__(256) void pack_tiles_kernel(const bf16_t* __restrict__ W, int rows, int K,
+                                                         bf16_t* __restrict__ Wt) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int KT = K / 64;
+  const size_t groups = (size_t)(rows + 31) / 32;
+  if (idx >= groups * KT * 32 * 8) return;
+  const int c = (int)(idx % 8);           // 16-byte piece within the 64-deep row segment
+  const int r = (int)((idx / 8) % 32);    // row within the group
+  const size_t gk = idx / 256;            // group * KT + K-tile
+  const int kt = (int)(gk % KT), row = (int)(gk / KT) * 32 + r;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < rows) v = *(const u32x4_t*)(W + (size_t)row * K + kt * 64 + c * 8);
+  *(u32x4_t*)(Wt + idx * 8) = v;
+}
+
 template <bool PAIRED, class Map, class Epi>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
                                                             int splits, int M, int part_ld,
@@ -617,8 +637,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ---- launch helpers ---------------------------------------------------------------------
 template <int BM, int BN, int BKT, int WMW, int WNW, int S, bool PAIRED, class Map, class Epi>
-void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, const bf16_t* w, Map map, int ncols,
-                int nw, Epi epi, float* part, hipStream_t st) {
+void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, const bf16_t* w, int tiled, Map map,
+                int ncols, int nw, Epi epi, float* part, hipStream_t st) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   constexpr int XR = gemm_extra_rows(BM, BN, BKT, WMW * WNW, PAIRED);
   // the extended-tile kernel only where the plan folds leftover rows into the
@@ -626,31 +646,33 @@ void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, cons
   if constexpr (XR > 0) {
     if (pl.ext) {
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, XR, PAIRED, Map, Epi>), dim3(grid),
-                         dim3(64 * WMW * WNW), 0, st, a, lda, M, K, w, nw, map, ncols, epi, part, nw, pl.m_tiles,
-                         pl.n_tiles, pl.splits);
+                         dim3(64 * WMW * WNW), 0, st, a, lda, M, K, w, nw, tiled, map, ncols, epi, part, nw,
+                         pl.m_tiles, pl.n_tiles, pl.splits);
       return;
     }
   }
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, 0, PAIRED, Map, Epi>), dim3(grid), dim3(64 * WMW * WNW),
-                     0, st, a, lda, M, K, w, nw, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
+                     0, st, a, lda, M, K, w, nw, tiled, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
 }
 
 template <bool PAIRED, class Map, class Epi>
-hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int K, const void* W, Map map,
+hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int K, const Wt& W, Map map,
                          int ncols, int nw, Epi epi, float* partial, hipStream_t st, const char* tag,
                          bool reduce = true) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   if (grid == 0) return hipSuccess;
   // buffer descriptors address at most 4 GiB per operand
-  if ((size_t)M * lda * 2 > 0xffffffffull || (size_t)nw * K * 2 > 0xffffffffull) return hipErrorInvalidValue;
+  if ((size_t)M * lda * 2 > 0xffffffffull || (size_t)(nw + 31) / 32 * 32 * K * 2 > 0xffffffffull)
+    return hipErrorInvalidValue;
   const bf16_t* a = (const bf16_t*)A;
-  const bf16_t* w = (const bf16_t*)W;
+  const int tiled = W.tiled != nullptr && K % 64 == 0;
+  const bf16_t* w = (const bf16_t*)(tiled ? W.tiled : W.w);
   float* part = pl.splits > 1 ? partial : nullptr;
   {
     ProfScope prof(tag, st);
     switch (pl.cfg) {
 #define FPD_CFG(E, BM, BN, BKT, WMW, WNW, S) \
-  case E: launch_cfg<BM, BN, BKT, WMW, WNW, S, PAIRED>(pl, a, lda, M, K, w, map, ncols, nw, epi, part, st); break;
+  case E: launch_cfg<BM, BN, BKT, WMW, WNW, S, PAIRED>(pl, a, lda, M, K, w, tiled, map, ncols, nw, epi, part, st); break;
       FPD_GEMM_CFGS(FPD_CFG)
 #undef FPD_CFG
       default: return hipErrorInvalidValue;
@@ -666,7 +688,7 @@ hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int 
 }
 
 template <bool PAIRED, class Map, class Epi>
-hipError_t run_bf16(const void* A, int lda, int M, int K, const void* W, Map map, int ncols, int nw, Epi epi,
+hipError_t run_bf16(const void* A, int lda, int M, int K, const Wt& W, Map map, int ncols, int nw, Epi epi,
                     float* partial, size_t partial_bytes, hipStream_t st, const char* tag) {
   GemmPlan pl = plan_gemm_bf16(M, ncols, K, nw, PAIRED);
   if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) {
@@ -677,8 +699,9 @@ hipError_t run_bf16(const void* A, int lda, int M, int K, const void* W, Map map
 }
 
 template <bool PAIRED, class Map, class Epi>
-hipError_t run_f32(const void* A, int lda, int M, int K, const void* W, Map map, int ncols, Epi epi,
+hipError_t run_f32(const void* A, int lda, int M, int K, const Wt& Wm, Map map, int ncols, Epi epi,
                    hipStream_t st, const char* tag) {
+  const void* W = Wm.w;
   ProfScope prof(tag, st);
   const int m_tiles = (M + 63) / 64;
   const int n_tiles = (ncols + (PAIRED ? 31 : 63)) / (PAIRED ? 32 : 64);
@@ -761,7 +784,17 @@ GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   return with_splits(GEMM_64x128_S3, 256, 640);
 }
 
-hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const void* W, int N,
+size_t gemm_tiles_elems(int rows, int K) { return (size_t)(rows + 31) / 32 * 32 * (size_t)K; }
+
+hipError_t gemm_pack_tiles(const void* W, int rows, int K, void* Wtiled, hipStream_t st) {
+  if (rows <= 0 || K <= 0 || K % 64) return hipErrorInvalidValue;
+  const size_t n = gemm_tiles_elems(rows, K) / 8;
+  hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const bf16_t*)W, rows,
+                     K, (bf16_t*)Wtiled);
+  return hipGetLastError();
+}
+
+hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const Wt& W, int N,
                           float* out, int ldo, float* partial, size_t partial_bytes, hipStream_t st,
                           const char* tag) {
   EpiStore e{out, ldo};
@@ -770,7 +803,7 @@ hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const vo
   return run_f32<false>(A, lda, M, K, W, MapPlain{}, N, e, st, tag);
 }
 
-hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const void* W, int N,
+hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const Wt& W, int N,
                          float* h, int ldh, float* partial, size_t partial_bytes, hipStream_t st,
                          const char* tag) {
   EpiResid e{h, ldh};
@@ -779,7 +812,7 @@ hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const voi
   return run_f32<false>(A, lda, M, K, W, MapPlain{}, N, e, st, tag);
 }
 
-hipError_t gemm_residual_norm(int dt, const void* A, int M, int K, const void* W, int H, float* h, const void* g,
+hipError_t gemm_residual_norm(int dt, const void* A, int M, int K, const Wt& W, int H, float* h, const void* g,
                               float eps, void* out, int final_L, float* partial, size_t partial_bytes,
                               hipStream_t st, const char* tag) {
   if (dt == FPD_DTYPE_BF16) {
@@ -797,7 +830,7 @@ hipError_t gemm_residual_norm(int dt, const void* A, int M, int K, const void* W
   return residual_norm(dt, nullptr, 1, M, H, h, g, eps, out, final_L, st);
 }
 
-hipError_t gemm_qkv(int dt, const void* A, int M, int K, const void* Wqkv, const QkvOut& o,
+hipError_t gemm_qkv(int dt, const void* A, int M, int K, const Wt& Wqkv, const QkvOut& o,
                     float* partial, size_t partial_bytes, hipStream_t st) {
   const int half = o.d / 2;
   const int pairs = (o.nq + 2 * o.nkv) * half;
@@ -841,7 +874,7 @@ hipError_t gemm_qkv(int dt, const void* A, int M, int K, const void* Wqkv, const
   return run_f32<true>(A, K, M, K, Wqkv, MapRope{half}, pairs, e, st, "gemm_qkv");
 }
 
-hipError_t gemm_ctx_kv(int dt, const void* Zn, int M, int K, const void* Wkv, const CtxOut& o,
+hipError_t gemm_ctx_kv(int dt, const void* Zn, int M, int K, const Wt& Wkv, const CtxOut& o,
                        float* partial, size_t partial_bytes, hipStream_t st) {
   const int half = o.d / 2;
   const int pairs = 2 * o.nkv * half;
@@ -855,7 +888,7 @@ hipError_t gemm_ctx_kv(int dt, const void* Zn, int M, int K, const void* Wkv, co
   return run_f32<true>(Zn, K, M, K, Wkv, MapRope{half}, pairs, e, st, "gemm_ctx_kv");
 }
 
-hipError_t gemm_swiglu(int dt, const void* A, int M, int K, const void* Wgu, int I, void* u,
+hipError_t gemm_swiglu(int dt, const void* A, int M, int K, const Wt& Wgu, int I, void* u,
                        float* partial, size_t partial_bytes, hipStream_t st) {
   if (dt == FPD_DTYPE_BF16) {
     EpiGlu<bf16_t> e{(bf16_t*)u, I};

@@ -79,6 +79,7 @@ _lib.fpd_last_error.argtypes = []
 _lib.fpd_last_error.restype = ctypes.c_char_p
 _create = _proto("fpd_drafter_create", [ctypes.POINTER(fpd_config), ctypes.POINTER(fpd_weights), ctypes.POINTER(vp)])
 _destroy = _proto("fpd_drafter_destroy", [vp])
+_prepare = _proto("fpd_drafter_prepare", [vp, vp])
 _expand = _proto("fpd_schema_expand", [ctypes.POINTER(fpd_schema), i32, ctypes.POINTER(fpd_layout_sizes),
                                        P_i32, P_i32, P_i32, P_i32, P_i32])
 _lay_create = _proto("fpd_layout_create", [vp, ctypes.POINTER(fpd_schema), ctypes.POINTER(vp), P_i32])
@@ -212,6 +213,11 @@ def fpd_drafter_create(cfg: fpd_config, weights: Dict) -> Drafter:
 
 def fpd_drafter_destroy(d: Drafter) -> None:
     d.close()
+
+
+def fpd_drafter_prepare(d: Drafter, stream=None) -> None:
+    """Register-tile copies of the bf16 projections (no-op for f32)."""
+    _check(_prepare(d.handle, _stream(stream)), "fpd_drafter_prepare")
 
 
 def _schema_struct(schema: Dict):

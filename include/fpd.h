@@ -162,7 +162,20 @@ typedef struct fpd_layout fpd_layout;
  * only host memory.  Errors: E_ARG (null), E_DTYPE, E_SHAPE (non-positive
  * or inconsistent sizes), E_UNSUPPORTED (see fpd_config).                  */
 int32_t fpd_drafter_create(const fpd_config *cfg, const fpd_weights *w, fpd_drafter **out);
+/* Frees the drafter and the tile copies fpd_drafter_prepare made.        */
 int32_t fpd_drafter_destroy(fpd_drafter *d);
+
+/* Copies the bf16 projections (w_qkv, w_o, w_gu, w_d of every layer, and
+ * w_fc) into device memory owned by the drafter, K-tile-contiguous: within
+ * each group of 32 rows, the 64-column K-tiles are stored one after
+ * another, so each K step of a GEMM workgroup reads 4 KB-contiguous runs
+ * of weights instead of 128-byte pieces of rows that lie 2 K bytes apart.
+ * Later calls read the copies (same results: only the addresses change).
+ * The row-major weights stay borrowed (embed, w_lm and the norms are read
+ * from them).  No-op for F32 drafters and for a drafter already prepared.
+ * Allocating; synchronises `stream` (a hipStream_t, NULL = default).
+ * Errors: E_ARG (null), E_HIP.                                            */
+int32_t fpd_drafter_prepare(fpd_drafter *d, void *stream);
 
 /* Host only, no GPU call: expands a schema into its layout for vocabulary
  * size `vocab` (VFlash paper §2.3: position alignment -- each position's role
@@ -180,8 +193,9 @@ int32_t fpd_schema_expand(const fpd_schema *s, int32_t vocab, fpd_layout_sizes *
 /* Expands the schema (as fpd_schema_expand), uploads the layout tables and
  * gathers the legal W_lm rows of every set into one contiguous device
  * buffer, once per layout (so the constrained LM head streams only legal
- * rows).  This and fpd_drafter_create are the only allocating calls; this
- * one synchronises the device before returning.  *L_out receives L.       */
+ * rows).  This, fpd_drafter_create and fpd_drafter_prepare are the only
+ * allocating calls; this one synchronises the device before returning.
+ * *L_out receives L.                                                      */
 int32_t fpd_layout_create(const fpd_drafter *d, const fpd_schema *s, fpd_layout **out,
                           int32_t *L_out);
 int32_t fpd_layout_destroy(fpd_layout *lay);

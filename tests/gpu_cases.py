@@ -146,7 +146,7 @@ def check_tokens(got, want, gap, scale, dtype, what=""):
 class GpuCase:
     """One workload on the GPU through the C ABI."""
 
-    def __init__(self, wl: synth.Workload, inp: synth.Inputs, n_layers=None):
+    def __init__(self, wl: synth.Workload, inp: synth.Inputs, n_layers=None, prepare=True):
         from block_draft_decoding_amd import fpd
         self.fpd = fpd
         self.wl = wl
@@ -157,6 +157,8 @@ class GpuCase:
             w = replace(w, layers=w.layers[:n_layers])
         self.w = fpd.weights_to_device(w, self.dt)
         self.d = fpd.fpd_drafter_create(fpd.make_config(shape), self.w)
+        if prepare:
+            fpd.fpd_drafter_prepare(self.d)
         self.lay = fpd.fpd_layout_create(self.d, wl.schema)
         self.B, self.C, self.L = wl.batch, wl.ctx, self.lay.L
         self.shared = wl.shared_ctx

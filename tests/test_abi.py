@@ -169,6 +169,7 @@ def test_hot_calls_reject_bad_arguments_without_gpu_work():
         assert fpd._boxes(8, 8, None, 0.5, 1, 8, 8, 8, None) == fpd.FPD_E_ARG
         assert fpd._boxes(8, 8, 8, float("nan"), 1, 8, 8, 8, None) == fpd.FPD_E_ARG
         assert fpd._boxes(8, 8, 8, 0.5, 0, 8, 8, 8, None) == fpd.FPD_E_SHAPE
+        assert fpd._prepare(None, None) == fpd.FPD_E_ARG
     finally:
         fpd._destroy(h)
 
