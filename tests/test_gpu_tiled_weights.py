@@ -34,9 +34,11 @@ def test_tiled_copies_match_row_major_bitwise(B, L, C, inter):
     row = GpuCase(wl, inp, prepare=False)
     row.fuse()
     row.draft()
+    lg_row = row.argmax(logits=True)
     torch.cuda.synchronize()
     progress(f"[tiled-vs-row-major B={B} L={L} C={C}] comparing")
     assert torch.equal(g.hidden, row.hidden)
+    assert torch.equal(lg, lg_row) and torch.equal(g.toks, row.toks)
     if C > 0:  # the C written positions (the capacity is padded to a multiple of 8)
         for x, y in zip(g.ctx_np(), row.ctx_np()):
             assert np.array_equal(x, y)
