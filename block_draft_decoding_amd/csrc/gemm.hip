@@ -5,7 +5,9 @@
 // (one barrier per K-tile), split-K with a fixed-order reduction when the
 // tile count alone cannot fill 256 CUs, an XCD-aware tile order so the
 // workgroups that share a weight tile run on the same XCD, and a last row
-// tile that can carry up to 16 leftover rows.
+// tile that can carry up to 16 leftover rows.  W is read row-major or from
+// its K-tile-contiguous copy (Wt::tiled: each 32-row group's 64-deep K-tiles
+// back to back), which changes only the load addresses.
 //
 // "Paired" epilogues need two W rows per output (RoPE rotates column i with
 // column i + d/2 of a head; SwiGLU combines gate row i with up row I + i).
