@@ -29,10 +29,11 @@ constexpr int HST_WIDE = 3;
 constexpr int HST_NARROW = 4;
 constexpr int kCUs = 256;
 // K groups of a narrow-chunk item: the most (4, 2 or 1) that divide the K
-// tiles and keep K groups x items within one per CU
+// tiles and still run every item in one pass of workgroups (LDS holds one
+// four-group workgroup per CU, two two-group ones)
 int head_k_groups(int items, int H) {
-  for (int kw = 4; kw > 1; kw /= 2)
-    if ((long)items * kw <= kCUs && H % (BK * kw) == 0) return kw;
+  if (items <= kCUs && H % (BK * 4) == 0) return 4;
+  if (items <= 2 * kCUs && H % (BK * 2) == 0) return 2;
   return 1;
 }
 constexpr int FBM = 16;    // f32 path: rows per tile

@@ -66,8 +66,10 @@ def compare_all(wl, g, lg, res, dtype, name=""):
 
 
 # The constrained LM head takes 32-column chunks for all but the text cases;
-# their work items split K four ways (traj2d: 33 items), two ways (traj2d3d,
-# B = 2: 97 items) or not at all (traj2d3d, B = 4: 161 items).
+# their work items split K four ways (traj2d: 33 items; traj2d3d, B = 2: 97
+# and B = 4: 161 items); the full-size 2D+3D block (322 items) splits two
+# ways.  test_head_without_k_groups covers a hidden size whose K tiles
+# cannot be split.
 @pytest.mark.parametrize("kind,B,C,over", [
     ("text", 2, 300, dict(block_len=37)),
     ("traj2d3d", 2, 300, dict(n_points=7, off_id=4099 - 1020 + 1002)),
@@ -88,6 +90,15 @@ def test_small_bf16_end_to_end(kind, B, C, over):
     if kind == "traj2d3d":
         n_off = int((res["tokens"] == lay.off_id).sum())
         progress(f"[pairs] off-frame tokens {n_off} of {res['tokens'].size}")
+
+
+def test_head_without_k_groups():
+    """Hidden 320 = 5 K tiles: the narrow-chunk LM head cannot split K into
+    wave groups and runs one wave per item."""
+    shape = replace(SMALL, hidden=320)
+    wl = small_workload("traj2d3d", 2, 64, seed=74, shape=shape, n_points=7, off_id=4099 - 1020 + 1002)
+    inp, g, lg, res = run_both(wl)
+    compare_all(wl, g, lg, res, "bf16", "hidden 320")
 
 
 def test_more_than_eight_split_partials():
