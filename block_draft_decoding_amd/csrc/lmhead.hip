@@ -19,7 +19,7 @@ namespace {
 constexpr int BK = 64;
 constexpr int HBM = 32;    // rows per tile (bf16)
 constexpr int HBN = 128;   // columns per chunk (bf16): 4 waves x 32
-constexpr int HBN_NARROW = 32;  // one wave: for layouts whose 128-column chunks give few work items
+constexpr int HBN_NARROW = 32;  // one wave per K group: for layouts whose 128-column chunks give few items
 // depth of the global -> LDS ring (bf16): 3 for the wide chunks, so that two
 // workgroups fit in a CU's 160 KB of LDS (4 stages come to just over 80 KB
 // with the reduction arrays: 183 -> 148 us for a full-vocabulary text block,
