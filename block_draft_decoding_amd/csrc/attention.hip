@@ -15,7 +15,8 @@
 // P feeds O^T += V^T P^T with no data movement.  V is stored d-major
 // (transposed) so each V^T fragment is one 16-byte LDS read.  The key range
 // is split across workgroups when (b, kv-head, query-tile) alone cannot fill
-// the GPU; partial (m, l, O) are merged by a log-sum-exp combine.
+// the GPU; partial (m, l, O) (O as per-row-scaled fp16) are merged by a
+// log-sum-exp combine.
 #include <algorithm>
 
 #include "../../include/fpd.h"
@@ -36,11 +37,25 @@ constexpr int ASTAGE = KSLOTS + VSLOTS;
 constexpr int APT = KSLOTS / (AW * 64);  // K (and V) loads per thread and stage
 constexpr float kRescale = 8.0f;  // lazy rescale: keep the running max until it grows by 2^8
 
+// fp16 pairs (round to nearest even; the first value in the low half), built
+// from scalar conversions: a two-element _Float16 vector initialised from two
+// conversions came out with both words holding the first pair here.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ float f16lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
 struct AttnP {
   const bf16_t *q, *kb, *vbt, *ck, *cvt;
   bf16_t* o;
-  float* opart;   // [splits, B, nq, L, D]
-  float* mlpart;  // [splits, B, nq, L, 2]
+  uint16_t* opart;  // [splits, B, nq, L, D] fp16: each split's O / (l c), c = its row's max |O / l|
+  float* mlpart;    // [splits, B, nq, L, 4]: reference max (log2 units), l, c, unused
   int B, L, Lp, C, cap, nq, nkv, g, R, q_tiles, splits, ctx_tiles, blk_tiles, ctx_bstride;
   float scale_log2;
 };
@@ -246,27 +261,39 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
         *(u32x2_t*)(dst + d0) = w;
       }
   } else {
+    // The split's output is stored normalised and scaled into [-1, 1] by its
+    // row's largest magnitude c, in fp16 (11 significant bits, finer than the
+    // bf16 output): half the bytes of an f32 partial, the same accuracy.
     const size_t row = (((size_t)sp * p.B + b) * p.nq + head) * p.L + l;
-    float* dst = p.opart + row * D;
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[dt][r]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));  // the row's other 64 dims
+    const float c = amax > 0.f ? amax / l_tot : 1.0f;
+    const float inv = amax > 0.f ? 1.0f / amax : 1.0f;
+    uint16_t* dst = p.opart + row * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = dt * 32 + q4 * 8 + lg * 4;
-        *(f32x4_t*)(dst + d0) = f32x4_t{o[dt][q4 * 4], o[dt][q4 * 4 + 1], o[dt][q4 * 4 + 2], o[dt][q4 * 4 + 3]};
+        u32x2_t w;
+        w[0] = pack_f16x2(o[dt][q4 * 4 + 0] * inv, o[dt][q4 * 4 + 1] * inv);
+        w[1] = pack_f16x2(o[dt][q4 * 4 + 2] * inv, o[dt][q4 * 4 + 3] * inv);
+        *(u32x2_t*)(dst + d0) = w;
       }
-    if (lg == 0) {
-      p.mlpart[row * 2 + 0] = m_run * p.scale_log2;
-      p.mlpart[row * 2 + 1] = l_tot;
-    }
+    if (lg == 0) *(f32x4_t*)(p.mlpart + row * 4) = f32x4_t{m_run * p.scale_log2, l_tot, c, 0.f};
   }
 }
 
 // Merges split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, where
-// m_s is each split's reference max (log2 units).  8 rows per workgroup, 4
-// dims per thread; the NS splits' loads are all issued before any use.
+// m_s is each split's reference max (log2 units) and O_s = l_s c_s x_s with
+// x_s the stored fp16 values.  8 rows per workgroup, 4 dims per thread; the
+// NS splits' loads are all issued before any use.
 template <class T, int NS>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const uint16_t* __restrict__ opart,
                                                            const float* __restrict__ ml, int B, int nq, int L,
                                                            T* __restrict__ o) {
   const size_t rows = (size_t)B * nq * L;
@@ -276,14 +303,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int l = (int)(row % L);
   const size_t bh = row / L;
   const int head = (int)(bh % nq), b = (int)(bh / nq);
-  float ms[NS], ls[NS];
-  f32x4_t v[NS];
+  float ms[NS], ls[NS], cs[NS];
+  u32x2_t v[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const f32x2_t x = *(const f32x2_t*)(ml + (s * rows + row) * 2);
+    const f32x4_t x = *(const f32x4_t*)(ml + (s * rows + row) * 4);
     ms[s] = x[0];
     ls[s] = x[1];
-    v[s] = *(const f32x4_t*)(opart + (s * rows + row) * D + d0);
+    cs[s] = x[2];
+    v[s] = *(const u32x2_t*)(opart + (s * rows + row) * D + d0);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -295,7 +323,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     if (ms[s] == -INFINITY) continue;
     const float w = __builtin_amdgcn_exp2f(ms[s] - M);
     den += w * ls[s];
-    acc += w * v[s];
+    const float wl = w * ls[s] * cs[s];
+    acc[0] += wl * f16lo(v[s][0]);
+    acc[1] += wl * f16hi(v[s][0]);
+    acc[2] += wl * f16lo(v[s][1]);
+    acc[3] += wl * f16hi(v[s][1]);
   }
   const float inv = 1.0f / den;
   T* dst = o + ((size_t)b * L + l) * (size_t)(nq * D) + (size_t)head * D + d0;
@@ -393,7 +425,7 @@ size_t attention_scratch_bytes(int dt, int B, int L, int C, int nq, int nkv, int
   const int s = attn_splits(B, L, C, nq, nkv, nullptr, nullptr);
   if (s == 1) return 0;
   const size_t rows = (size_t)s * B * nq * L;
-  return rows * d * sizeof(float) + rows * 2 * sizeof(float);
+  return rows * d * sizeof(uint16_t) + rows * 4 * sizeof(float);
 }
 
 hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_bytes, hipStream_t st) {
@@ -412,11 +444,11 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     int total = 0;
     p.splits = attn_splits(a.B, a.L, a.C, a.nq, a.nkv, &p.q_tiles, &total);
     const size_t rows = (size_t)p.splits * a.B * a.nq * a.L;
-    if (p.splits > 1 && rows * (D + 2) * sizeof(float) > scratch_bytes) p.splits = 1;
+    if (p.splits > 1 && rows * (D * sizeof(uint16_t) + 4 * sizeof(float)) > scratch_bytes) p.splits = 1;
     p.ctx_tiles = (a.C + KT - 1) / KT;
     p.blk_tiles = (a.L + KT - 1) / KT;
-    p.opart = (float*)scratch;
-    p.mlpart = (float*)scratch + rows * D;
+    p.opart = (uint16_t*)scratch;
+    p.mlpart = (float*)((uint16_t*)scratch + rows * D);
     p.scale_log2 = a.scale * 1.4426950408889634f;
     const int grid = p.q_tiles * p.splits * a.B * a.nkv;
     {
