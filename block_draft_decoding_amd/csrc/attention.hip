@@ -290,49 +290,52 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
 
 // Merges split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, where
 // m_s is each split's reference max (log2 units) and O_s = l_s c_s x_s with
-// x_s the stored fp16 values.  8 rows per workgroup, 4 dims per thread; the
-// NS splits' loads are all issued before any use.
-template <class T, int NS>
+// x_s the stored fp16 values.  16 rows per workgroup, 8 dims per thread (one
+// 16-byte load per split, one 16-byte bf16 store); the NS splits' loads are
+// all issued before any use.
+template <int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const uint16_t* __restrict__ opart,
                                                            const float* __restrict__ ml, int B, int nq, int L,
-                                                           T* __restrict__ o) {
+                                                           bf16_t* __restrict__ o) {
   const size_t rows = (size_t)B * nq * L;
-  const size_t row = (size_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (row >= rows) return;
-  const int d0 = (threadIdx.x & 31) * 4;
+  const int d0 = (threadIdx.x & 15) * 8;
   const int l = (int)(row % L);
   const size_t bh = row / L;
   const int head = (int)(bh % nq), b = (int)(bh / nq);
   float ms[NS], ls[NS], cs[NS];
-  u32x2_t v[NS];
+  u32x4_t v[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const f32x4_t x = *(const f32x4_t*)(ml + (s * rows + row) * 4);
     ms[s] = x[0];
     ls[s] = x[1];
     cs[s] = x[2];
-    v[s] = *(const u32x2_t*)(opart + (s * rows + row) * D + d0);
+    v[s] = *(const u32x4_t*)(opart + (s * rows + row) * D + d0);
   }
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < NS; ++s) M = fmaxf(M, ms[s]);
   float den = 0.f;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (ms[s] == -INFINITY) continue;
     const float w = __builtin_amdgcn_exp2f(ms[s] - M);
     den += w * ls[s];
     const float wl = w * ls[s] * cs[s];
-    acc[0] += wl * f16lo(v[s][0]);
-    acc[1] += wl * f16hi(v[s][0]);
-    acc[2] += wl * f16lo(v[s][1]);
-    acc[3] += wl * f16hi(v[s][1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += wl * f16lo(v[s][j]);
+      acc[2 * j + 1] += wl * f16hi(v[s][j]);
+    }
   }
   const float inv = 1.0f / den;
-  T* dst = o + ((size_t)b * L + l) * (size_t)(nq * D) + (size_t)head * D + d0;
+  u32x4_t w;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) Elem<T>::st(dst + e, acc[e] * inv);
+  for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  *(u32x4_t*)(o + ((size_t)b * L + l) * (size_t)(nq * D) + (size_t)head * D + d0) = w;
 }
 
 // ---- f32 path: one wave per (b, head, query); keys split over lanes ------------------------
@@ -459,11 +462,11 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     if (e != hipSuccess || p.splits == 1) return e;
     ProfScope prof("attn_combine", st);
     const size_t nrows = (size_t)a.B * a.nq * a.L;
-    const dim3 cg((unsigned)((nrows + 7) / 8));
+    const dim3 cg((unsigned)((nrows + 15) / 16));
     switch (p.splits) {
 #define FPD_COMB(NS)                                                                                            \
   case NS:                                                                                                      \
-    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, NS>), cg, dim3(256), 0, st, p.opart, p.mlpart, a.B, a.nq, a.L, \
+    hipLaunchKernelGGL((attn_combine_kernel<NS>), cg, dim3(256), 0, st, p.opart, p.mlpart, a.B, a.nq, a.L,       \
                        (bf16_t*)a.o);                                                                          \
     break;
       FPD_COMB(2)
