@@ -244,16 +244,22 @@ int32_t fpd_drafter_prepare(fpd_drafter* d, void* stream) {
   if (e != hipSuccess) return fail(FPD_E_HIP, std::string("tiled weights: ") + hipGetErrorString(e));
   hipStream_t s = (hipStream_t)stream;
   bf16_t* p = (bf16_t*)buf;
+  // copies W [rows, K] to the next free place of the buffer and returns it
+  auto pack = [&](const void* W, int rows, int K, size_t elems) -> const void* {
+    const void* at = p;
+    if (e == hipSuccess) e = gemm_pack_tiles(W, rows, K, p, s);
+    p += elems;
+    return at;
+  };
   std::vector<const void*> tq, to, tg, td;
-  for (int li = 0; li < c.n_layers && e == hipSuccess; ++li) {
+  for (int li = 0; li < c.n_layers; ++li) {
     const fpd_layer_weights& lw = d->layers[li];
-    tq.push_back(p), e = gemm_pack_tiles(lw.w_qkv, nqkv, H, p, s), p += e_qkv;
-    if (e == hipSuccess) to.push_back(p), e = gemm_pack_tiles(lw.w_o, H, qd, p, s), p += e_o;
-    if (e == hipSuccess) tg.push_back(p), e = gemm_pack_tiles(lw.w_gu, 2 * c.inter, H, p, s), p += e_gu;
-    if (e == hipSuccess) td.push_back(p), e = gemm_pack_tiles(lw.w_d, H, c.inter, p, s), p += e_d;
+    tq.push_back(pack(lw.w_qkv, nqkv, H, e_qkv));
+    to.push_back(pack(lw.w_o, H, qd, e_o));
+    tg.push_back(pack(lw.w_gu, 2 * c.inter, H, e_gu));
+    td.push_back(pack(lw.w_d, H, c.inter, e_d));
   }
-  const void* tfc = p;
-  if (e == hipSuccess) e = gemm_pack_tiles(d->w.w_fc, H, c.n_fused * H, p, s);
+  const void* tfc = pack(d->w.w_fc, H, c.n_fused * H, e_fc);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     (void)hipFree(buf);
@@ -511,8 +517,7 @@ int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32
     FPD_TRY_HIP(attention(dt, at, wsp(ws, w.attn), w.attn_bytes, s));
     // h += O W_o^T, a = RMSNorm(h) for the MLP
     FPD_TRY_HIP(gemm_residual_norm(dt, at.o, M, qd, Wt{lw.w_o, tl ? d->t_o[li] : nullptr}, H, h, lw.g_mlp, c.rms_eps,
-                                   a, 0, part, w.partial_bytes, s,
-                                   "gemm_o"));
+                                   a, 0, part, w.partial_bytes, s, "gemm_o"));
     void* u = wsp(ws, w.u);
     FPD_TRY_HIP(gemm_swiglu(dt, a, M, H, Wt{lw.w_gu, tl ? d->t_gu[li] : nullptr}, c.inter, u, part, w.partial_bytes,
                             s));
