@@ -262,8 +262,8 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
       }
   } else {
     // The split's output is stored normalised and scaled into [-1, 1] by its
-    // row's largest magnitude c, in fp16 (11 significant bits, finer than the
-    // bf16 output): half the bytes of an f32 partial, the same accuracy.
+    // row's largest magnitude c, in fp16: 11 significant bits relative to c,
+    // finer than the bf16 output it becomes, in half the bytes of f32.
     const size_t row = (((size_t)sp * p.B + b) * p.nq + head) * p.L + l;
     float amax = 0.f;
 #pragma unroll
