@@ -137,8 +137,8 @@ __device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, i
 // c ^ ((row / (16 / CH)) % CH): the MFMA operand reads (16 rows x 16 bytes
 // per LDS cycle) then hit distinct banks.  The swizzle is applied by choosing which
 // global chunk each lane loads.  Lanes whose row lies outside the problem
-// load a clamped in-range row instead of being switched off, so every wave
-// issues the same number of loads per stage and vmcnt counts stay exact; the
+// load a clamped in-range row instead of being switched off, so every loading
+// wave issues the same number of loads per stage and vmcnt counts stay exact; the
 // outputs of those rows/columns are never stored.
 //
 // When M = k BM + r with 0 < r <= XR, the last row tile also carries the r
@@ -153,22 +153,28 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     int splits) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int NT = 64 * NW;
+  // Waves that fill the ring.  In 8-wave workgroups only waves 0-3 (one per
+  // SIMD) issue the loads and wait for them: the other wave of each SIMD keeps
+  // issuing MFMAs meanwhile (2-4% faster than all eight loading; 4-wave
+  // workgroups were slower that way).
+  constexpr int LW = NW == 8 ? NW / 2 : NW;
+  constexpr int LT = 64 * LW;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int CH = BK / 8;        // 16-byte chunks per tile row
-  constexpr int AI = BM * CH / NT;  // load instructions per wave and stage (A)
-  constexpr int BI = BN * CH / NT;  // (B)
+  constexpr int AI = BM * CH / LT;  // load instructions per wave and stage (A)
+  constexpr int BI = BN * CH / LT;  // (B)
   constexpr int LPS = AI + BI;
   static_assert(BK == 32 || BK == 64, "K tile");
-  static_assert(TM >= 1 && TN >= 1 && AI >= 1 && BI >= 1 && BM * CH % NT == 0 && BN * CH % NT == 0, "tile shape");
+  static_assert(TM >= 1 && TN >= 1 && AI >= 1 && BI >= 1 && BM * CH % LT == 0 && BN * CH % LT == 0, "tile shape");
   static_assert(!PAIRED || (TN % 2 == 0), "paired epilogues need an even number of N sub-tiles");
   static_assert(STAGES >= 2 && STAGES <= 8 && LPS * (STAGES - 1) < 64, "pipeline depth");
   constexpr int CPT = PAIRED ? BN / 2 : BN;  // logical columns per tile
   static_assert(XR == 0 || XR == gemm_extra_rows(BM, BN, BK, NW, PAIRED), "extra rows of this tile shape");
-  constexpr int XI = XR * BK * 2 / (NW * 256);  // 4-byte loads per wave and stage for the extra rows
+  constexpr int XI = XR * BK * 2 / (LW * 256);  // 4-byte loads per wave and stage for the extra rows
   constexpr int XB = XR ? CPT / (NW * 16) : 0;  // 16-column blocks (pairs when PAIRED) per wave
   constexpr int XA = PAIRED ? 2 * XB : XB;      // their accumulators
-  static_assert(XR == 0 || (XI >= 1 && XI * NW * 256 == XR * BK * 2 && XB * NW * 16 == CPT), "extra rows");
+  static_assert(XR == 0 || (XI >= 1 && XI * LW * 256 == XR * BK * 2 && XB * NW * 16 == CPT), "extra rows");
   constexpr int AR = BM + XR;                // A rows held per stage
   constexpr int STAGE = (AR + BN) * CH;      // 16-byte slots per stage
 
@@ -177,6 +183,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const bool loader = wave < LW;
   const int tile = gemm_tile_order(blockIdx.x, gridDim.x, m_tiles, M / BM);
   const int mt = tile % m_tiles;
   const int rest = tile / m_tiles;
@@ -232,6 +239,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   auto issue = [&](int kt, int stage, auto ext_c) {
     const int soff = kt * BK * 2;
     const int k0 = kt * BK, sb = w_tiled ? (k0 / 64) * 4096 + (k0 % 64) * 2 : soff;
+    if (!loader) return;
     u32x4_t* base = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < AI; ++i) lds_dma16(arsrc, base + (wave * AI + i) * 64, aoff[i], soff);
@@ -280,7 +288,8 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   // The ring holds STAGES K-tiles.  Within a K-tile the operand fragments of
   // step kk+1 are read from LDS while the MFMAs of step kk run (two register
   // sets, order pinned by scheduling barriers).  At the last step each wave
-  // drains its own LDS reads and waits for its loads of the next K-tile; one
+  // drains its own LDS reads and each loading wave waits for its loads of the
+  // next K-tile; one
   // barrier then hands the finished stage back to the loads (K-tile kt +
   // STAGES goes into it) and publishes the next K-tile, whose first fragments
   // are read before the last MFMAs of the current one.
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     };
     if (kt0 >= kt1) return;
     wait_lgkm0();
-    wait_stages<LPSX, STAGES - 1>(min(STAGES - 1, kt1 - 1 - kt0));
+    if (loader) wait_stages<LPSX, STAGES - 1>(min(STAGES - 1, kt1 - 1 - kt0));
     barrier_nofence();
     fetch(0, 0, 0);
     for (int kt = kt0; kt < kt1; ++kt) {
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
           fetch(stage, kk + 1, (kk + 1) & 1);
         } else {
           wait_lgkm0();
-          if (kt + 1 < kt1) wait_stages<LPSX, STAGES - 2>(min(STAGES - 2, kt1 - 2 - kt));
+          if (loader && kt + 1 < kt1) wait_stages<LPSX, STAGES - 2>(min(STAGES - 2, kt1 - 2 - kt));
           barrier_nofence();
           if (kt + STAGES < kt1) issue(kt + STAGES, stage, ext_c);
           if (kt + 1 < kt1) fetch(stage + 1 == STAGES ? 0 : stage + 1, 0, 0);
