@@ -23,7 +23,8 @@ namespace fpd {
   X(GEMM_128x256_W8_S2, 128, 256, 64, 2, 4, 2) \
   X(GEMM_128x256_W8_S3, 128, 256, 64, 2, 4, 3) \
   X(GEMM_256x128_W8_S3, 256, 128, 64, 4, 2, 3) \
-  X(GEMM_128x256_W8_K32_S5, 128, 256, 32, 2, 4, 5)
+  X(GEMM_128x256_W8_K32_S5, 128, 256, 32, 2, 4, 5) \
+  X(GEMM_128x128_W8_S3, 128, 128, 64, 4, 2, 3)
 enum GemmCfg {
 #define FPD_ENUM(name, ...) name,
   FPD_GEMM_CFGS(FPD_ENUM)
