@@ -4,9 +4,9 @@ only the addresses the GEMMs load from, so its outputs must equal those of
 the same drafter unprepared bit for bit, and the oracle within the bf16
 bar.  The cases cover every GEMM plan the drafter takes: few rows (split K
 over 32-row tiles), up to 64 rows, a last 128-row tile that carries
-leftover rows, partly filled tiles, a ragged last column tile (an MLP width
-that is not a multiple of the tile) and a context long enough for the
-large-tile fusion path."""
+leftover rows, partly filled tiles, 128x128 tiles of 8 waves for a few
+hundred rows, a ragged last column tile (an MLP width that is not a multiple
+of the tile) and a context long enough for the large-tile fusion path."""
 from dataclasses import replace
 
 import numpy as np
@@ -25,6 +25,7 @@ pytestmark = pytest.mark.gpu
     (2, 25, 77, 1472),     # 50 rows; ragged MLP columns
     (1, 129, 200, 1408),   # one leftover row carried by the last tile; context 200 rows
     (2, 100, 600, 1472),   # 200 rows (partly filled last tile); context 1200 rows
+    (2, 150, 64, 1408),    # 300 rows: 128x128 8-wave tiles, K split (gate/up via the split-K sum)
 ])
 def test_tiled_copies_match_row_major_bitwise(B, L, C, inter):
     shape = replace(SMALL, inter=inter)
