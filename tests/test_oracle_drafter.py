@@ -30,39 +30,55 @@ def _rope_c(x, pos, theta):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def _torch_reference(s, W, feats, tokens, ctx_pos0=0):
+def _no_store(name, x):
+    return x
+
+
+def _torch_reference(s, W, feats, tokens, ctx_pos0=0, store=_no_store, want_ctx=False):
     """The drafter written with torch.nn.functional routines (no code shared
     with the oracle): linear, rms_norm, scaled_dot_product_attention with
-    grouped KV heads, silu, and RoPE as a complex rotation."""
+    grouped KV heads, silu, and RoPE as a complex rotation.  store(name, x)
+    is applied to each named intermediate ("zn", "ck", "cv", "a", "q",
+    "kb", "vb", "o", "mm", "u", "hf") right after it is computed: the
+    identity for full precision, a bf16 rounding to model storage points."""
     t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
     H, nq, nkv, d = s.hidden, s.n_q, s.n_kv, s.head_dim
     f = t(feats)
     B, nt, C, _ = f.shape
     X = f.permute(0, 2, 1, 3).reshape(B, C, nt * H)
-    Zn = F.rms_norm(F.linear(X, t(W.w_fc)), (H,), t(W.g_fc), eps=s.rms_eps)
+    Zn = store("zn", F.rms_norm(F.linear(X, t(W.w_fc)), (H,), t(W.g_fc), eps=s.rms_eps))
     cpos = torch.arange(C, dtype=torch.float64) + ctx_pos0
     L = tokens.shape[1]
     bpos = torch.arange(L, dtype=torch.float64) + C + ctx_pos0
-    outs = []
+    outs, cks, cvs = [], [], []
     for b in range(B):
         h = t(W.embed)[torch.from_numpy(np.asarray(tokens[b], np.int64))]
+        ckb, cvb = [], []
         for lw in W.layers:
             wq, wk, wv = torch.split(t(lw["w_qkv"]), [nq * d, nkv * d, nkv * d])
-            kc = _rope_c(F.linear(Zn[b], wk).reshape(C, nkv, d), cpos, s.rope_theta)
-            vc = F.linear(Zn[b], wv).reshape(C, nkv, d)
-            a = F.rms_norm(h, (H,), t(lw["g_attn"]), eps=s.rms_eps)
-            q = _rope_c(F.linear(a, wq).reshape(L, nq, d), bpos, s.rope_theta)
-            kb = _rope_c(F.linear(a, wk).reshape(L, nkv, d), bpos, s.rope_theta)
-            vb = F.linear(a, wv).reshape(L, nkv, d)
+            kc = store("ck", _rope_c(F.linear(Zn[b], wk).reshape(C, nkv, d), cpos, s.rope_theta))
+            vc = store("cv", F.linear(Zn[b], wv).reshape(C, nkv, d))
+            ckb.append(kc)
+            cvb.append(vc)
+            a = store("a", F.rms_norm(h, (H,), t(lw["g_attn"]), eps=s.rms_eps))
+            q = store("q", _rope_c(F.linear(a, wq).reshape(L, nq, d), bpos, s.rope_theta))
+            kb = store("kb", _rope_c(F.linear(a, wk).reshape(L, nkv, d), bpos, s.rope_theta))
+            vb = store("vb", F.linear(a, wv).reshape(L, nkv, d))
             kk = torch.cat([kc, kb]).permute(1, 0, 2)[None]
             vv = torch.cat([vc, vb]).permute(1, 0, 2)[None]
             o = F.scaled_dot_product_attention(q.permute(1, 0, 2)[None], kk, vv, enable_gqa=True)
-            h = h + F.linear(o[0].permute(1, 0, 2).reshape(L, nq * d), t(lw["w_o"]))
-            mm = F.rms_norm(h, (H,), t(lw["g_mlp"]), eps=s.rms_eps)
+            o = store("o", o[0].permute(1, 0, 2).reshape(L, nq * d))
+            h = h + F.linear(o, t(lw["w_o"]))
+            mm = store("mm", F.rms_norm(h, (H,), t(lw["g_mlp"]), eps=s.rms_eps))
             g, u = torch.split(F.linear(mm, t(lw["w_gu"])), [s.inter, s.inter], dim=-1)
-            h = h + F.linear(F.silu(g) * u, t(lw["w_d"]))
-        outs.append(F.rms_norm(h[1:], (H,), t(W.g_final), eps=s.rms_eps))
-    return torch.stack(outs).numpy()
+            h = h + F.linear(store("u", F.silu(g) * u), t(lw["w_d"]))
+        outs.append(store("hf", F.rms_norm(h[1:], (H,), t(W.g_final), eps=s.rms_eps)))
+        cks.append(torch.stack(ckb))
+        cvs.append(torch.stack(cvb))
+    hid = torch.stack(outs).numpy()
+    if want_ctx:   # [n_layers, B, C, n_kv, d], the oracle's layout
+        return hid, torch.stack(cks, 1).numpy(), torch.stack(cvs, 1).numpy()
+    return hid
 
 
 def _inputs(s, B=2, C=13, L=9, seed=5):
@@ -217,3 +233,78 @@ def test_shared_context_equals_separate_runs():
         np.testing.assert_array_equal(h[b], hb[0])
     # blocks differing only in their anchor still differ: the anchor matters
     assert not np.allclose(h[0], h[1])
+
+
+# --- where the bf16 drafter rounds (storage points of the bf16 workloads) -----------
+
+STORE_POINTS = ("zn", "ck", "cv", "a", "q", "kb", "vb", "o", "mm", "u", "hf")
+
+
+def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
+    """Nearest bfloat16 of float64 values (ties to even), written on the
+    float64 bit pattern: bfloat16 keeps 7 of float64's 52 stored mantissa
+    bits, so add half of bit 45's weight minus one plus bit 45 itself (the
+    round-half-even bias) and clear bits 0..44.  Exact for magnitudes in
+    bfloat16's normal range, which covers every value of these tests."""
+    u = x.contiguous().view(torch.int64)
+    bias = ((u >> 45) & 1) + ((1 << 44) - 1)
+    return ((u + bias) & ~((1 << 45) - 1)).view(torch.float64)
+
+
+def test_bit_pattern_bf16_rounding_hand_values():
+    v = torch.tensor([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 2 - 2.0 ** -10, -(1 + 2.0 ** -7),
+                      1 + 2.0 ** -8 + 2.0 ** -40, -(3 + 2.0 ** -7), 0.0], dtype=torch.float64)
+    want = [1.0, 1 + 2.0 ** -6, 2.0, -(1 + 2.0 ** -7), 1 + 2.0 ** -7, -3.0, 0.0]
+    assert _bf16_bits(v).tolist() == want
+
+
+def _bf16_case(seed=11):
+    s = _shape(dtype="bf16")
+    m = O.Model(s, synth.make_weights(s, seed))
+    feats, tokens = _inputs(s, B=2, C=13, L=9, seed=5)
+    return s, m, feats, tokens
+
+
+def _store_at(points):
+    def store(name, x):
+        return _bf16_bits(x) if name in points else x
+    return store
+
+
+def test_bf16_rounding_points_match_an_independent_composition():
+    """The oracle's bf16 drafter equals the torch composition rounded to
+    bf16 at exactly the storage points: the fused context rows and their
+    K/V, the normed inputs of the attention and MLP projections, Q/K/V after
+    RoPE, the attention output, the SwiGLU product and the final hidden
+    state; nowhere else."""
+    s, m, feats, tokens = _bf16_case()
+    ck, cv = O.fuse_context_kv(m, feats)
+    hid = O.draft_block(m, tokens, ck, cv)
+    want, wk, wv = _torch_reference(s, m.w, feats, tokens, store=_store_at(STORE_POINTS), want_ctx=True)
+    np.testing.assert_allclose(ck, wk, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cv, wv, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(hid, want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("dropped", STORE_POINTS)
+def test_each_rounding_point_is_visible(dropped):
+    """Removing any one rounding point from the composition moves the
+    outputs well past the agreement above, so an oracle missing that
+    rounding (or rounding one more tensor) fails the previous test."""
+    s, m, feats, tokens = _bf16_case()
+    ck, cv = O.fuse_context_kv(m, feats)
+    hid = O.draft_block(m, tokens, ck, cv)
+    got, gk, gv = _torch_reference(s, m.w, feats, tokens, store=_store_at(set(STORE_POINTS) - {dropped}),
+                                   want_ctx=True)
+    diff = max(np.abs(hid - got).max() / np.abs(hid).max(), np.abs(ck - gk).max() / np.abs(ck).max(),
+               np.abs(cv - gv).max() / np.abs(cv).max())
+    assert diff > 1e-5, (dropped, diff)
+
+
+def test_residual_stream_is_not_rounded():
+    """Rounding the residual stream too (one more storage point) would be
+    visible: the oracle keeps h at full precision between layers."""
+    s, m, feats, tokens = _bf16_case()
+    ck, cv = O.fuse_context_kv(m, feats)
+    _, res = O.draft_block(m, tokens, ck, cv, return_residuals=True)
+    assert not np.array_equal(res, O.bf16_round(res))
