@@ -13,7 +13,10 @@
 // read with bits 2 and 3 of the row index swapped, which makes the S^T
 // accumulator come out exactly in the B-operand layout of the next MFMA, so
 // P feeds O^T += V^T P^T with no data movement.  V is stored d-major
-// (transposed) so each V^T fragment is one 16-byte LDS read.  The key range
+// (transposed) so each V^T fragment is one 16-byte LDS read, and as fp16
+// holding the bf16-rounded values exactly, so that P enters that product in
+// fp16 (11 significant bits) rather than bf16 (8) at the same MFMA rate.
+// The key range
 // is split across workgroups when (b, kv-head, query-tile) alone cannot fill
 // the GPU; partial (m, l, O) (O as per-row-scaled fp16) are merged by a
 // log-sum-exp combine.
@@ -52,7 +55,8 @@ __device__ __forceinline__ float f16hi(uint32_t v) {
 }
 
 struct AttnP {
-  const bf16_t *q, *kb, *vbt, *ck, *cvt;
+  const bf16_t *q, *kb, *ck;
+  const uint16_t *vbt, *cvt;  // values as fp16 (bf16-rounded values, exactly)
   bf16_t* o;
   uint16_t* opart;  // [splits, B, nq, L, D] fp16: each split's O / (l c), c = its row's max |O / l|
   float* mlpart;    // [splits, B, nq, L, 4]: reference max (log2 units), l, c, unused
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
     if (t + AST - 1 < t1) issue(t + AST - 1, (t - t0 + AST - 1) % AST);
     if (wave_active) {
       const bf16x8_t* Kb = (const bf16x8_t*)Ks;
-      const bf16x8_t* Vb = (const bf16x8_t*)Vs;
+      const f16x8_t* Vh = (const f16x8_t*)Vs;
       f32x16_t s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -228,17 +232,19 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
           s[kb][r] = e;
           l_run += e;
         }
+      // P in fp16 (values in [0, 2^kRescale]; 11 significant bits) against
+      // the fp16 values, which hold the bf16-rounded V exactly
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          bf16x8_t pf;
+          f16x8_t pf;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[kb][h * 8 + e];
+          for (int e = 0; e < 8; ++e) pf[e] = (_Float16)s[kb][h * 8 + e];
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Vb[vslot(dt * 32 + lq, kb * 4 + h * 2 + lg)], pf,
-                                                            o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Vh[vslot(dt * 32 + lq, kb * 4 + h * 2 + lg)], pf,
+                                                           o[dt], 0, 0, 0);
         }
     }
   }
@@ -436,9 +442,9 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     AttnP p{};
     p.q = (const bf16_t*)a.q;
     p.kb = (const bf16_t*)a.kb;
-    p.vbt = (const bf16_t*)a.vbt;
+    p.vbt = (const uint16_t*)a.vbt;
     p.ck = (const bf16_t*)a.ck;
-    p.cvt = (const bf16_t*)a.cvt;
+    p.cvt = (const uint16_t*)a.cvt;
     p.o = (bf16_t*)a.o;
     p.B = a.B, p.L = a.L, p.Lp = a.Lp, p.C = a.C, p.cap = a.cap, p.nq = a.nq, p.nkv = a.nkv;
     p.ctx_bstride = a.ctx_bstride;

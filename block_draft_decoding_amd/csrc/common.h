@@ -9,6 +9,7 @@ namespace fpd {
 
 typedef uint16_t bf16_t;  // raw IEEE bfloat16 bits
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -30,6 +31,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Attention values of bf16 drafters: the value is rounded to bfloat16 (its
+// storage precision) and kept as the IEEE half with the same value, so the
+// P V product can take fp16 probabilities (11 significant bits instead of
+// 8) at the bf16 MFMA rate.  Exact for |v| in [2^-17, 65504]; smaller
+// magnitudes keep fp16's subnormal spacing 2^-24, larger ones overflow.
+__device__ __forceinline__ uint16_t bf16_value_as_f16(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)bf2f(f2bf(v)));
+}
+
 // Element load/store in the storage type, arithmetic in float.
 template <class T>
 struct Elem;
@@ -42,6 +52,19 @@ template <>
 struct Elem<bf16_t> {
   static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
   static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Store of an attention value (V, block or context): f32 drafters keep
+// float; bf16 drafters keep the bf16-rounded value as fp16 (above).
+template <class T>
+struct ValueStore;
+template <>
+struct ValueStore<float> {
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <>
+struct ValueStore<bf16_t> {
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = bf16_value_as_f16(v); }
 };
 
 // Maps a linear block index to a tile index so that consecutive tiles land

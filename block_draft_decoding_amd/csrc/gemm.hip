@@ -70,8 +70,8 @@ struct EpiQkv {
       Elem<T>::st(dst + i + half, x1);
     } else {
       T* dst = vt + ((size_t)b * nkv + (head - nq - nkv)) * d * Lp + l;
-      Elem<T>::st(dst + (size_t)i * Lp, x0);
-      Elem<T>::st(dst + (size_t)(i + half) * Lp, x1);
+      ValueStore<T>::st(dst + (size_t)i * Lp, x0);
+      ValueStore<T>::st(dst + (size_t)(i + half) * Lp, x1);
     }
   }
 };
@@ -91,8 +91,8 @@ struct EpiCtx {
       Elem<T>::st(dst + i + half, x1);
     } else {
       T* dst = vt + ((size_t)b * nkv + (head - nkv)) * d * cap + c;
-      Elem<T>::st(dst + (size_t)i * cap, x0);
-      Elem<T>::st(dst + (size_t)(i + half) * cap, x1);
+      ValueStore<T>::st(dst + (size_t)i * cap, x0);
+      ValueStore<T>::st(dst + (size_t)(i + half) * cap, x1);
     }
   }
 };
@@ -192,7 +192,10 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   const int m0 = mt * BM, c0 = nt * CPT;
   const int KT = K / BK;
   const int kt0 = (int)((long)ks * KT / splits), kt1 = (int)((long)(ks + 1) * KT / splits);
-  const bool ext = XR > 0 && m0 + BM < M;  // the last row tile carries rows BM .. BM + XR - 1
+  // only the plan's last row tile carries the rows past m_tiles * BM (any
+  // other tile would compute the next tile's first rows a second time, and a
+  // residual epilogue would add them twice)
+  const bool ext = XR > 0 && mt == m_tiles - 1 && m0 + BM < M;
 
   // Operands are read through buffer descriptors: the per-lane byte offset
   // (row and swizzled chunk) is fixed, the K-tile offset is a scalar.  The
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(const float* __restrict
   if (m >= M) return;
   const int b = m / e.L, l = m - b * e.L;
   bf16_t* dst = e.vt + ((size_t)b * e.nkv + (head - e.nq - e.nkv)) * D * e.Lp + l;
-  for (int dd = tid / RB; dd < D; dd += 256 / RB) dst[(size_t)dd * e.Lp] = f2bf(vt[dd][r]);
+  for (int dd = tid / RB; dd < D; dd += 256 / RB) dst[(size_t)dd * e.Lp] = bf16_value_as_f16(vt[dd][r]);
 }
 
 // ---- f32 SIMT kernel (the fp32 drafter) -----------------------------------------------

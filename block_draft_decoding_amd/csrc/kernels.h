@@ -11,7 +11,8 @@
 namespace fpd {
 
 // Brackets the kernel launches of its lifetime with HIP events on `st` when
-// per-launch timing is enabled (fpd_profile_enable); otherwise a no-op.
+// per-launch timing is enabled (fpd_profile_enable); otherwise a no-op that
+// reads one atomic flag (no lock).
 class ProfScope {
  public:
   ProfScope(const char* tag, hipStream_t st);

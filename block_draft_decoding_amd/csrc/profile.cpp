@@ -3,6 +3,7 @@
 // launch's own stream; the caller reads the durations after synchronising.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -18,8 +19,8 @@ struct Rec {
   hipEvent_t a, b;
 };
 
-std::mutex g_mu;
-bool g_on = false;
+std::mutex g_mu;                  // guards the records and the event pool
+std::atomic<bool> g_on{false};    // read without the lock on every launch
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;  // events kept for reuse until the process ends
 
@@ -45,8 +46,9 @@ void recycle_all() {
 }  // namespace
 
 ProfScope::ProfScope(const char* tag, hipStream_t st) : st_(st), idx_(-1) {
+  if (!g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return;
+  if (!g_on.load(std::memory_order_relaxed)) return;
   Rec r{tag, take_event(), take_event()};
   if (!r.a || !r.b) return;
   if (hipEventRecord(r.a, st) != hipSuccess) return;
@@ -69,7 +71,7 @@ extern "C" {
 int32_t fpd_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_mu);
   recycle_all();
-  g_on = on != 0;
+  g_on.store(on != 0, std::memory_order_relaxed);
   return FPD_OK;
 }
 

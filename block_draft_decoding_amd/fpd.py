@@ -168,6 +168,11 @@ class Drafter:
     def dtype(self) -> torch.dtype:
         return TORCH_DT[self.cfg.dtype]
 
+    @property
+    def value_dtype(self) -> torch.dtype:
+        """dtype of the context values ctx_v: float16 for bf16 drafters."""
+        return torch.float16 if self.dtype == torch.bfloat16 else self.dtype
+
     def close(self) -> None:
         if getattr(self, "handle", None):
             _destroy(self.handle)
@@ -306,11 +311,14 @@ def alloc_workspace(d: Drafter, B: int, C: int, L: int, device=None) -> torch.Te
 
 
 def alloc_context(d: Drafter, B: int, cap: int, device=None):
-    """ctx_k [n_layers, B, n_kv, cap, d] and ctx_v [n_layers, B, n_kv, d, cap]."""
+    """ctx_k [n_layers, B, n_kv, cap, d] (drafter dtype) and ctx_v
+    [n_layers, B, n_kv, d, cap] (float16 for bf16 drafters: the bf16-rounded
+    values held exactly; float32 for f32 drafters)."""
     c = d.cfg
-    kw = dict(dtype=d.dtype, device=device or "cuda")
-    return (torch.empty(c.n_layers, B, c.n_kv, cap, c.head_dim, **kw),
-            torch.empty(c.n_layers, B, c.n_kv, c.head_dim, cap, **kw))
+    dev = device or "cuda"
+    vdt = d.value_dtype
+    return (torch.empty(c.n_layers, B, c.n_kv, cap, c.head_dim, dtype=d.dtype, device=dev),
+            torch.empty(c.n_layers, B, c.n_kv, c.head_dim, cap, dtype=vdt, device=dev))
 
 
 # ---- hot path ------------------------------------------------------------------
@@ -320,7 +328,7 @@ def fpd_fuse_context_kv(d: Drafter, feats: torch.Tensor, ctx_k: torch.Tensor, ct
     B, nt, C, H = feats.shape
     cap = ctx_k.shape[3]
     _check(_fuse(d.handle, _ptr(feats, "feats", d.dtype), B, C, pos0, _ptr(ctx_k, "ctx_k", d.dtype),
-                 _ptr(ctx_v, "ctx_v", d.dtype), cap, _ptr(ws, "ws"), ws.numel(), _stream(stream)),
+                 _ptr(ctx_v, "ctx_v", d.value_dtype), cap, _ptr(ws, "ws"), ws.numel(), _stream(stream)),
            "fpd_fuse_context_kv")
 
 
@@ -330,7 +338,7 @@ def fpd_append_context_kv(d: Drafter, feats: torch.Tensor, ctx_k: torch.Tensor, 
     B, nt, C_new, H = feats.shape
     cap = ctx_k.shape[3]
     _check(_append(d.handle, _ptr(feats, "feats", d.dtype), B, C_new, pos0, _ptr(ctx_k, "ctx_k", d.dtype),
-                   _ptr(ctx_v, "ctx_v", d.dtype), cap, _ptr(ws, "ws"), ws.numel(), _stream(stream)),
+                   _ptr(ctx_v, "ctx_v", d.value_dtype), cap, _ptr(ws, "ws"), ws.numel(), _stream(stream)),
            "fpd_append_context_kv")
 
 
@@ -340,7 +348,7 @@ def fpd_draft_block(d: Drafter, tokens: torch.Tensor, ctx_k: Optional[torch.Tens
     B, L = tokens.shape
     cap = ctx_k.shape[3] if ctx_k is not None else 0
     _check(_draft(d.handle, _ptr(tokens, "tokens", torch.int32), B, L, _ptr(ctx_k, "ctx_k", d.dtype),
-                  _ptr(ctx_v, "ctx_v", d.dtype), C, cap, C if block_pos is None else block_pos,
+                  _ptr(ctx_v, "ctx_v", d.value_dtype), C, cap, C if block_pos is None else block_pos,
                   _ptr(hidden_out, "hidden_out", d.dtype), _ptr(ws, "ws"), ws.numel(), _stream(stream)),
            "fpd_draft_block")
 
@@ -353,7 +361,7 @@ def fpd_draft_blocks_shared_ctx(d: Drafter, tokens: torch.Tensor, ctx_k: torch.T
     B, L = tokens.shape
     cap = ctx_k.shape[3]
     _check(_draft_shared(d.handle, _ptr(tokens, "tokens", torch.int32), B, L, _ptr(ctx_k, "ctx_k", d.dtype),
-                         _ptr(ctx_v, "ctx_v", d.dtype), C, cap, C if block_pos is None else block_pos,
+                         _ptr(ctx_v, "ctx_v", d.value_dtype), C, cap, C if block_pos is None else block_pos,
                          _ptr(hidden_out, "hidden_out", d.dtype), _ptr(ws, "ws"), ws.numel(), _stream(stream)),
            "fpd_draft_blocks_shared_ctx")
 

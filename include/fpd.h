@@ -217,8 +217,12 @@ int32_t fpd_workspace_size(const fpd_drafter *d, int32_t B, int32_t C, int32_t L
  *   K_c = RoPE(Zn Wk_l^T) at positions pos0 .. pos0 + C - 1, V_c = Zn Wv_l^T,
  * where Wk_l / Wv_l are the K / V rows of layer l's w_qkv.
  * Writes keys 0..C-1 of ctx_k [n_layers, B, n_kv, ctx_cap, d] DT (keys
- * stored after RoPE) and of ctx_v [n_layers, B, n_kv, d, ctx_cap] DT (values
- * stored d-major, so attention reads them along keys).  ctx_cap >= C and a
+ * stored after RoPE) and of ctx_v [n_layers, B, n_kv, d, ctx_cap] (values
+ * stored d-major, so attention reads them along keys).  ctx_v's element type
+ * is the value type VT: float for F32 drafters; for BF16 drafters IEEE fp16
+ * holding each value rounded to bf16 (exact for |v| in [2^-17, 65504];
+ * larger magnitudes overflow), so that attention multiplies fp16
+ * probabilities with them.  ctx_cap >= C and a
  * multiple of 8.  Entries at keys >= C are left untouched and may hold
  * anything (they never reach an output of fpd_draft_block).               */
 int32_t fpd_fuse_context_kv(const fpd_drafter *d, const void *feats, int32_t B, int32_t C,
