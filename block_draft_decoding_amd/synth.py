@@ -80,7 +80,12 @@ class Workload:
     ctx: int
     schema: Dict
     seed_index: int
-    off_row_std: Optional[float] = None   # std of the OFF row of the LM head, if drawn apart
+    # std of the LM head's OFF row when it is drawn apart from the other rows.  The
+    # masked positions' final hidden states are strongly aligned (one MASK input
+    # token at every position), so OFF's logit moves together across positions;
+    # at 0.3 (15x the other rows) OFF wins 7 of the 64 image-coordinate pairs of
+    # the 64-waypoint block and 4 pairs need the joint decision.
+    off_row_std: Optional[float] = None
     k_star: Optional[List[int]] = None    # planted accepted lengths for text verification
     notes: str = ""
     shared_ctx: bool = False              # all blocks share one context (features of batch 1)
@@ -143,7 +148,7 @@ WORKLOADS: Dict[str, Workload] = {
                        notes="NAVSIM-shaped 2D trajectory, 8 waypoints x (x, y, delim), L=25"),
     "traj2d3d": Workload("traj2d3d", DRAFTER_4B, batch=1, ctx=4096,
                          schema=dict(kind="traj2d3d", n_points=64, **_bf16_ids(off_id=OFF_ID)),
-                         seed_index=4, off_row_std=0.06,
+                         seed_index=4, off_row_std=0.3,
                          notes="Alpamayo-shaped 2D+3D trajectory, 64 waypoints x "
                                "(u, v, X, Y, Z, delim), L=385, paired off-frame rule"),
     "flashdrive8": Workload("flashdrive8", DRAFTER_2L, batch=1, ctx=8,

@@ -15,20 +15,37 @@ import torch
 from block_draft_decoding_amd import synth
 from oracle import fpd_oracle as O
 
-# Parity rules (derivation in the repository's design notes):
-#  * TOL: relative L2 error ||g - o|| / ||o|| of every position's vector
-#    (hidden state, legal logits, context row; positions with >= 16 entries)
-#    and of the whole tensor: the stated 2e-2 (bf16) / 1e-4 (fp32);
-#  * ELEM: elementwise outlier guard |g - o| <= ELEM * max(|o|, rms(o));
-#  * GAP: argmax must agree wherever the oracle's top-2 legal-logit gap
-#    exceeds GAP * rms of that position's legal logits.  In bf16 two faithful
-#    implementations differ by ~1% rms in the logits (the oracle disagrees
-#    with itself at gaps up to ~2e-2 when only its attention probabilities
-#    are rounded to bf16), so 5e-2 is the bf16 threshold; disagreements
-#    between 1e-2 and it are counted and reported, not failed.
+# Parity rules (the derivation is in the repository's design notes).
+#  * TOL: north_star's "2e-2 relative" (bf16) / "1e-4" (fp32), read per vector:
+#    for every hidden row, context K/V row and position's legal logits,
+#    ||g - o|| / max(||o||, ||s||) <= TOL, where s holds the entries' natural
+#    scales: for the logit of id t at position p, s = ||h_p|| ||w_t|| / sqrt(H)
+#    (the rms of h_p . w_t over directions of h_p), so a delimiter's single
+#    legal logit, or the OFF logit of a row drawn 15x wider, is measured on
+#    its own scale; no scale for other tensors.  Legal sets of fewer than 16
+#    ids are compared per id across the positions that use them
+#    (rel_close_logits).  The whole tensor is held to the same bound.
+#  * ELEM: elementwise guard |g - o| <= ELEM * max(|o|, s) (s as above; the
+#    tensor's rms where no scale is given).  bf16: a second faithful
+#    implementation that only accumulates in float32 instead of float64 (same
+#    bf16 storage points) already reaches 3.5e-2 (hidden) and 3.7e-2 (logits)
+#    on the 385-position block, with 4,279 hidden values past 2e-2, because
+#    every bf16 storage point turns a tiny pre-rounding difference into
+#    whole-ulp flips of some elements (tests/golden/noise_floor_traj2d3d.json);
+#    the guard is 0.1, under 3x that.
+#  * Tokens given the same hidden states (the LM head, masked argmax and
+#    pairing alone): the benchmark spec as written -- ids agree wherever the oracle's
+#    top-2 legal gap exceeds GAP_HEAD = 1e-2.
+#  * Tokens end to end (bf16): the same float32-accumulating implementation
+#    flips a token at a top-2 gap of 0.021, so a 1e-2 gate cannot hold for any
+#    float32-accumulating path; ids must agree wherever the gap exceeds
+#    GAP_E2E = 5e-2 of the position's legal-logit rms (~4 standard deviations of
+#    the floor's top-2 logit difference), and disagreements with gaps between
+#    1e-2 and that are counted and reported.  fp32 workloads use 1e-2.
 TOL = {"bf16": 2e-2, "f32": 1e-4}
-ELEM = {"bf16": 2e-1, "f32": 1e-4}
-GAP = {"bf16": 5e-2, "f32": 1e-2}
+ELEM = {"bf16": 0.1, "f32": 1e-4}
+GAP_HEAD = 1e-2
+GAP_E2E = {"bf16": 5e-2, "f32": 1e-2}
 GAP_REPORT = 1e-2
 
 _LOG = os.path.join(os.environ.get("GRAFT_REPO_ROOT", "."), "gpurun_out", "test_progress.log")
@@ -60,16 +77,12 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
-def rel_close(got, want, dtype, what=""):
-    """Relative-error checks over the finite entries (the non-finite pattern,
-    i.e. the -inf padding of logits, must match exactly):
-      * per position with >= 16 entries: ||g - o|| / ||o|| <= TOL[dtype];
-      * the whole tensor: ||g - o|| / ||o|| <= TOL[dtype];
-      * every entry: |g - o| <= ELEM[dtype] * max(|o|, rms(o)).
-    Positions with fewer entries (a delimiter's single legal logit) are a
-    handful of scalars whose relative error is a single noise sample; the
-    whole-tensor and elementwise checks cover them.  Returns (max per-position
-    relative error, max elementwise error relative to max(|o|, rms))."""
+def rel_close(got, want, dtype, what="", scale=None):
+    """The TOL and ELEM rules over the finite entries (the non-finite pattern,
+    i.e. the -inf padding of logits, must match exactly).  The last axis is
+    the vector; scale (optional, same shape as want) holds each entry's
+    natural scale s.  Returns (max per-vector relative error, max elementwise
+    error relative to max(|o|, s))."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
@@ -79,68 +92,193 @@ def rel_close(got, want, dtype, what=""):
     w2 = np.where(fin, want, 0.0).reshape(-1, want.shape[-1])
     g, w = got[fin], want[fin]
     rms = np.sqrt(np.mean(w * w)) if w.size else 0.0
-    nfin = fin.reshape(-1, want.shape[-1]).sum(axis=1)
-    big = nfin >= 16
-    num = np.linalg.norm(g2 - w2, axis=1)[big]
-    den = np.linalg.norm(w2, axis=1)[big]
-    row = num / np.maximum(den, 1e-300)
+    keep = fin.reshape(-1, want.shape[-1]).any(axis=1)
+    num = np.linalg.norm(g2 - w2, axis=1)
+    den = np.linalg.norm(w2, axis=1)
+    whole_den = np.linalg.norm(w)
+    floor = np.full(w.shape, rms)
+    if scale is not None:
+        sc = np.where(fin, np.asarray(scale, np.float64), 0.0)
+        assert sc.shape == want.shape, (what, sc.shape)
+        den = np.maximum(den, np.linalg.norm(sc.reshape(-1, want.shape[-1]), axis=1))
+        whole_den = max(whole_den, float(np.linalg.norm(sc)))
+        floor = sc[fin]
+    row = (num / np.maximum(den, 1e-300))[keep]
     rmax = float(row.max()) if row.size else 0.0
-    whole = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-300)) if w.size else 0.0
-    elem = np.abs(g - w) / np.maximum(np.abs(w), rms) if w.size else np.zeros(0)
+    whole = float(np.linalg.norm(g - w) / max(whole_den, 1e-300)) if w.size else 0.0
+    elem = np.abs(g - w) / np.maximum(np.maximum(np.abs(w), floor), 1e-300) if w.size else np.zeros(0)
     emax = float(elem.max()) if elem.size else 0.0
-    assert rmax <= TOL[dtype], f"{what}: per-position relative error {rmax:.3e} > {TOL[dtype]}"
+    assert rmax <= TOL[dtype], f"{what}: per-vector relative error {rmax:.3e} > {TOL[dtype]}"
     assert whole <= TOL[dtype], f"{what}: whole-tensor relative error {whole:.3e} > {TOL[dtype]}"
-    assert emax <= ELEM[dtype], f"{what}: elementwise error {emax:.3e} > {ELEM[dtype]} (rms {rms:.3g})"
+    assert emax <= ELEM[dtype], f"{what}: elementwise error {emax:.3e} > {ELEM[dtype]}"
     return max(rmax, whole), emax
 
 
-def top2_gap(z: np.ndarray, lay: O.Layout) -> np.ndarray:
-    """Gap between the two largest legal logits of every position [B, L-1]."""
-    B = z.shape[0]
-    gap = np.empty((B, lay.L - 1))
+SMALL_SET = 16
+
+
+def rel_close_logits(got, want, lay: O.Layout, dtype, what="", scale=None):
+    """rel_close for gathered legal logits [B, L-1, W] (scale: same shape).
+    A position whose legal set has SMALL_SET ids or more is one vector; the
+    logits of a smaller set (a delimiter's single id, a sign's two, a digit
+    slot's eleven) are compared per id across every position of a request
+    that uses the set, one vector per (request, set, id): a relative error
+    needs more than a handful of samples to mean anything.  The whole tensor
+    and every element are checked as in rel_close."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    B = want.shape[0]
+    sc = np.ones(want.shape) if scale is None else np.asarray(scale, np.float64)
+    sizes = np.array([len(lay.legal(p)) for p in range(1, lay.L)])
+    big = np.nonzero(sizes >= SMALL_SET)[0]
+    gv, wv, sv = [], [], []
+    if big.size:
+        for a, out in ((got, gv), (want, wv), (sc, sv)):
+            out.append(a[:, big].reshape(-1, want.shape[-1]))
+    for sidx in sorted(set(int(lay.pos_set[p + 1]) for p in np.nonzero(sizes < SMALL_SET)[0])):
+        ps = [p - 1 for p in range(1, lay.L) if int(lay.pos_set[p]) == sidx]
+        n = len(lay.sets[sidx])
+        for a, out in ((got, gv), (want, wv), (sc, sv)):
+            out.append(a[:, ps, :n].transpose(0, 2, 1).reshape(B * n, len(ps)))
+    width = max(v.shape[1] for v in wv)   # vectors padded with -inf, which the checks skip
+    pad = lambda a: np.pad(a, ((0, 0), (0, width - a.shape[1])), constant_values=-np.inf)
+    return rel_close(np.concatenate([pad(a) for a in gv]), np.concatenate([pad(a) for a in wv]), dtype, what,
+                     scale=None if scale is None else np.concatenate([pad(a) for a in sv]))
+
+
+def logit_scale(hidden: np.ndarray, w_lm: np.ndarray, lay: O.Layout) -> np.ndarray:
+    """Natural scale of every gathered legal logit [B, L-1, W]:
+    ||h_p|| ||w_t|| / sqrt(H) for id t at position p (0 in the padding)."""
+    h = np.asarray(hidden, np.float64)
+    B, P, H = h.shape
+    hn = np.linalg.norm(h, axis=-1)
+    width = max(len(lay.legal(p)) for p in range(1, lay.L))
+    out = np.zeros((B, P, width))
+    norms = {}
+    for p in range(1, lay.L):
+        key = int(lay.pos_set[p])
+        if key not in norms:
+            ids = lay.legal(p)
+            wn = np.empty(len(ids))
+            for lo in range(0, len(ids), 1 << 14):
+                blk = np.asarray(w_lm[ids[lo:lo + (1 << 14)]], np.float64)
+                wn[lo:lo + len(blk)] = np.linalg.norm(blk, axis=1)
+            norms[key] = wn / np.sqrt(H)
+        wn = norms[key]
+        out[:, p - 1, :len(wn)] = hn[:, p - 1, None] * wn[None, :]
+    return out
+
+
+def legal_logits(hidden: np.ndarray, w_lm: np.ndarray, lay: O.Layout) -> np.ndarray:
+    """Oracle logits of the legal ids only, float64: [B, L-1, V] with -inf at
+    illegal ids would be large, so this returns the gathered layout
+    ([B, L-1, W], ascending ids, -inf padding) computed row set by row set.
+    Equal to O.gathered_logits(O.full_logits(...)) (pinned on the CPU)."""
+    h = np.asarray(hidden, np.float64)
+    B, P, H = h.shape
+    width = max(len(lay.legal(p)) for p in range(1, lay.L))
+    out = np.full((B, P, width), -np.inf)
+    by_set = {}
+    for p in range(1, lay.L):
+        by_set.setdefault(int(lay.pos_set[p]), []).append(p)
+    for s, ps in by_set.items():
+        ids = lay.legal(ps[0])
+        idx = np.array(ps) - 1
+        for lo in range(0, len(ids), 1 << 14):
+            w = np.asarray(w_lm[ids[lo:lo + (1 << 14)]], np.float64)
+            out[:, idx, lo:lo + len(w)] = h[:, idx] @ w.T
+    return out
+
+
+def tokens_from_legal(zg: np.ndarray, lay: O.Layout) -> np.ndarray:
+    """The oracle's constrained tokens (masked argmax, then the pairing rule)
+    computed from gathered legal logits: the union U of all legal ids is a
+    compact vocabulary (ascending, so ids keep their order and ties their
+    lowest-id winner), and the decision runs on z restricted to U."""
+    U = np.unique(np.concatenate([lay.legal(p) for p in range(1, lay.L)]))
+    pos = {int(u): i for i, u in enumerate(U)}
+    B, P, _ = zg.shape
+    zc = np.full((B, P, len(U)), -np.inf)
+    sets = [[pos[int(i)] for i in s] for s in lay.sets]
     for p in range(1, lay.L):
         ids = lay.legal(p)
-        if lay.pairs and lay.off_id in ids:
-            ids = ids[ids != lay.off_id]
-        v = z[:, p - 1, ids]
-        if v.shape[1] < 2:
-            gap[:, p - 1] = np.inf
-            continue
-        part = np.partition(v, -2, axis=1)
-        gap[:, p - 1] = part[:, -1] - part[:, -2]
-    for (pu, pv) in lay.pairs:   # the pair decision margin also has to be clear
+        zc[:, p - 1, [pos[int(i)] for i in ids]] = zg[:, p - 1, :len(ids)]
+    ps = [int(x) for x in lay.pos_set]
+    if any(x == -1 for x in ps):
+        raise ValueError("free positions: use the full logits")
+    off = pos.get(int(lay.off_id), -1) if lay.off_id is not None and lay.off_id >= 0 else -1
+    schema = dict(kind="custom", block_len=lay.L, sets=sets, pos_set=ps, pairs=lay.pairs, fields=[], off_id=off,
+                  fill_id=-1, digit0_id=-1, coord_base=0, coord_count=0)
+    small = O.build_layout(schema, len(U))
+    return U[O.constrained_tokens(zc, small)].astype(np.int32)
+
+
+def top2_gap(z: np.ndarray, lay: O.Layout, gathered: bool = False) -> np.ndarray:
+    """Decision margin of every position [B, L-1]: the gap between the two
+    largest legal logits (OFF excluded at paired positions), and at paired
+    positions also |on-frame pair score - (OFF, OFF) score|.  z: full
+    logits [B, L-1, V], or gathered legal logits when gathered is set."""
+    B = z.shape[0]
+    gap = np.empty((B, lay.L - 1))
+
+    def vals(b, p, ids_sel=None):
+        ids = lay.legal(p)
+        row = z[b, p - 1, :len(ids)] if gathered else z[b, p - 1, ids]
+        if ids_sel is not None:
+            row = row[ids_sel(ids)]
+        return row
+
+    not_off = lambda ids: ids != lay.off_id
+    for p in range(1, lay.L):
+        ids = lay.legal(p)
+        sel = not_off if (lay.pairs and lay.off_id in ids) else None
         for b in range(B):
-            A = lay.legal(pu)
-            A = A[A != lay.off_id]
-            Bs = lay.legal(pv)
-            Bs = Bs[Bs != lay.off_id]
-            on = z[b, pu - 1, A].max() + z[b, pv - 1, Bs].max()
-            off = z[b, pu - 1, lay.off_id] + z[b, pv - 1, lay.off_id]
+            v = vals(b, p, sel)
+            if v.shape[0] < 2:
+                gap[b, p - 1] = np.inf
+                continue
+            part = np.partition(v, -2)
+            gap[b, p - 1] = part[-1] - part[-2]
+    for (pu, pv) in lay.pairs:   # the pair decision margin also has to be clear
+        iu = int(np.searchsorted(lay.legal(pu), lay.off_id))
+        iv = int(np.searchsorted(lay.legal(pv), lay.off_id))
+        for b in range(B):
+            on = vals(b, pu, not_off).max() + vals(b, pv, not_off).max()
+            off = vals(b, pu)[iu] + vals(b, pv)[iv]
             g = min(gap[b, pu - 1], gap[b, pv - 1], abs(on - off))
             gap[b, pu - 1] = gap[b, pv - 1] = g
     return gap
 
 
-def legal_rms(z: np.ndarray, lay: O.Layout) -> np.ndarray:
+def legal_rms(z: np.ndarray, lay: O.Layout, gathered: bool = False) -> np.ndarray:
     """rms of each position's legal logits [B, L-1]."""
     out = np.empty(z.shape[:2])
     for p in range(1, lay.L):
-        v = z[:, p - 1, lay.legal(p)]
+        ids = lay.legal(p)
+        v = z[:, p - 1, :len(ids)] if gathered else z[:, p - 1, ids]
         out[:, p - 1] = np.sqrt(np.mean(v * v, axis=1))
     return out
 
 
-def check_tokens(got, want, gap, scale, dtype, what=""):
-    """Token ids must agree wherever gap > GAP[dtype] * scale.  Returns
-    (agreeing positions, disagreements with gap > GAP_REPORT, disagreements
-    below it)."""
+def check_tokens(got, want, gap, threshold, what=""):
+    """Token ids must agree wherever gap > threshold (a scalar or one value
+    per position).  Returns (agreeing positions, disagreements with
+    gap > GAP_REPORT, disagreements at or below it)."""
     got = np.asarray(got)
     want = np.asarray(want)
-    clear = gap > GAP[dtype] * scale
+    clear = gap > threshold
     bad = clear & (got != want)
     assert not bad.any(), f"{what}: {int(bad.sum())} clear-gap token mismatches at {np.argwhere(bad)[:5]}"
     diff = got != want
     return int((~diff).sum()), int((diff & (gap > GAP_REPORT)).sum()), int((diff & (gap <= GAP_REPORT)).sum())
+
+
+def check_tokens_e2e(got, want, z, lay, dtype, what="", gathered=False):
+    """End-to-end token rule (GAP_E2E); returns check_tokens' counts."""
+    gap = top2_gap(z, lay, gathered)
+    thr = GAP_E2E[dtype] * legal_rms(z, lay, gathered) if dtype == "bf16" else GAP_E2E[dtype]
+    return check_tokens(got, want, gap, thr, what)
 
 
 class GpuCase:
@@ -220,3 +358,30 @@ def oracle_result(name: str):
     res = O.run_block(m, inp.feats, inp.tokens, wl.schema, want_logits=True, shared_ctx=wl.shared_ctx)
     progress(f"[oracle] {name} done in {time.time() - t:.1f}s")
     return res
+
+def head_stage(hidden_gpu: np.ndarray, w_lm: np.ndarray, lay: O.Layout, vocab: int):
+    """The oracle's LM head, masked argmax and pairing on the GPU's own hidden
+    states: (gathered legal logits [B, L-1, W], tokens [B, L-1])."""
+    h = np.asarray(hidden_gpu, np.float64)
+    if any(int(x) == -1 for x in lay.pos_set[1:]):
+        z = np.empty(h.shape[:2] + (vocab,))
+        for lo in range(0, vocab, 1 << 14):
+            z[:, :, lo:lo + (1 << 14)] = h @ np.asarray(w_lm[lo:lo + (1 << 14)], np.float64).T
+        return O.gathered_logits(z, lay), O.constrained_tokens(z, lay)
+    zg = legal_logits(h, w_lm, lay)
+    return zg, tokens_from_legal(zg, lay)
+
+
+def check_head_stage(g: "GpuCase", lg, lay: O.Layout, w_lm, dtype: str, what=""):
+    """Given the same hidden states (the GPU's), the GPU's legal logits must
+    meet TOL / ELEM and its tokens must equal the oracle's wherever the top-2
+    gap exceeds GAP_HEAD.  Returns (logit errors, token counts)."""
+    hid = to_np(g.hidden)
+    zg, toks = head_stage(hid, w_lm, lay, g.wl.shape.vocab)
+    errs = None
+    if lg is not None:
+        errs = rel_close_logits(to_np(lg), zg, lay, dtype, f"{what} head logits",
+                                scale=logit_scale(hid, w_lm, lay))
+    gap = top2_gap(zg, lay, gathered=True)
+    cnt = check_tokens(g.toks.cpu().numpy(), toks, gap, GAP_HEAD, f"{what} head tokens")
+    return errs, cnt

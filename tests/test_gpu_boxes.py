@@ -61,7 +61,7 @@ def _legal_tokens(lay, B, rng, n_bad):
 def test_small_box_block_end_to_end():
     wl = small_workload("boxes2d", 3, 77, seed=70, n_points=9)
     inp, g, lg, res = run_both(wl)
-    compare_all(wl, g, lg, res, "bf16", "small boxes")
+    compare_all(wl, g, lg, res, "bf16", "small boxes", inp.weights.w_lm)
     lay = res["layout"]
     toks = g.toks.cpu().numpy()
     P = lay.L - 1
@@ -135,7 +135,7 @@ def test_full_size_box_list():
     torch.cuda.synchronize()
     progress(f"[gpu] {name} done")
     res = oracle_result(name)
-    compare_all(wl, g, lg, res, "bf16", f"full {name}")
+    compare_all(wl, g, lg, res, "bf16", f"full {name}", inp.weights.w_lm)
     lay = res["layout"]
     toks = g.toks.cpu().numpy()
     conf = synth.make_box_conf(wl.batch, lay.L - 1, 4000 + wl.seed_index)

@@ -1,9 +1,14 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
-same seeded inputs.  Bit-exact for token ids, masks and accepted lengths;
-floating point within 2e-2 (bf16) / 1e-4 (fp32) relative in the form
-|g - o| <= tol * max(|o|, rms(o)); argmax agreement wherever the oracle's
-top-2 legal-logit gap exceeds 1e-2."""
+same seeded inputs.  Bit-exact for token ids, masks and accepted lengths.
+Floating point: every hidden row, context row and position's legal logits
+within 2e-2 (bf16) / 1e-4 (fp32) relative per vector, with an elementwise
+guard; the LM head, masked argmax and pairing on the GPU's own hidden states
+must give the oracle's ids wherever the top-2 legal gap exceeds 1e-2; end to
+end (through five bf16 layers) ids must agree wherever the gap exceeds 5e-2
+of the position's legal-logit rms, and closer disagreements are counted.
+tests/gpu_cases.py states the rules and their derivation."""
 import itertools
+import time
 from dataclasses import replace
 
 import numpy as np
@@ -12,8 +17,9 @@ import torch
 
 from block_draft_decoding_amd import synth
 from oracle import fpd_oracle as O
-from tests.gpu_cases import (GpuCase, check_tokens, legal_rms, oracle_result, progress, rel_close,
-                             small_ids, to_np, top2_gap, workload_inputs)
+from tests.gpu_cases import (GpuCase, check_head_stage, check_tokens_e2e, legal_logits, logit_scale,
+                             oracle_result, progress, rel_close, rel_close_logits, small_ids, to_np,
+                             tokens_from_legal, workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +36,7 @@ def small_workload(kind, B, C, seed, shape=SMALL, shared_ctx=False, **schema_ove
 
 
 def run_both(wl, n_layers=None, logits=True):
+    """GPU run and oracle run of one workload: (inputs, GpuCase, logits, oracle result)."""
     inp = synth.make_inputs(wl)
     g = GpuCase(wl, inp, n_layers=n_layers)
     g.fuse()
@@ -43,7 +50,10 @@ def run_both(wl, n_layers=None, logits=True):
     return inp, g, lg, res
 
 
-def compare_all(wl, g, lg, res, dtype, name=""):
+def compare_all(wl, g, lg, res, dtype, name="", w_lm=None):
+    """Every parity rule on one run: context K/V, hidden states, legal
+    logits and tokens end to end, then the head stage on the GPU's own
+    hidden states (w_lm given), and legality of every id."""
     stats = {}
     if wl.ctx > 0:
         ck, cv = g.ctx_np()
@@ -52,16 +62,23 @@ def compare_all(wl, g, lg, res, dtype, name=""):
     stats["hidden"] = rel_close(to_np(g.hidden), res["hidden"], dtype, "hidden")
     lay = res["layout"]
     if lg is not None:
-        stats["logits"] = rel_close(to_np(lg), O.gathered_logits(res["logits"], lay), dtype, "logits")
-    gap = top2_gap(res["logits"], lay)
+        sc = logit_scale(res["hidden"], w_lm, lay) if w_lm is not None else None
+        stats["logits"] = rel_close_logits(to_np(lg), O.gathered_logits(res["logits"], lay), lay, dtype, "logits",
+                                           scale=sc)
     got = g.toks.cpu().numpy()
-    stats["tokens"] = check_tokens(got, res["tokens"], gap, legal_rms(res["logits"], lay), dtype, "tokens")
+    stats["tokens"] = check_tokens_e2e(got, res["tokens"], res["logits"], lay, dtype, "tokens")
+    if w_lm is not None:
+        herr, hcnt = check_head_stage(g, lg, lay, w_lm, dtype, name)
+        if herr is not None:
+            stats["head logits"] = herr
+        stats["head tokens"] = hcnt
     for b in range(got.shape[0]):
         for p in range(1, lay.L):
             assert got[b, p - 1] in lay.legal(p)
     progress(f"[parity {name}] " + ", ".join(
-        f"{k}: row {v[0]:.2e} elem {v[1]:.2e}" for k, v in stats.items() if k != "tokens") +
-        f"; tokens agree/differ(gap>1e-2)/differ(near tie) {stats['tokens']}")
+        f"{k}: row {v[0]:.2e} elem {v[1]:.2e}" for k, v in stats.items() if "tokens" not in k) +
+        f"; tokens agree/differ(gap>1e-2)/differ(gap<=1e-2) end to end {stats['tokens']}" +
+        (f", head stage {stats['head tokens']}" if "head tokens" in stats else ""))
     return stats
 
 
@@ -81,7 +98,7 @@ def compare_all(wl, g, lg, res, dtype, name=""):
 def test_small_bf16_end_to_end(kind, B, C, over):
     wl = small_workload(kind, B, C, seed=40 + B, **over)
     inp, g, lg, res = run_both(wl)
-    compare_all(wl, g, lg, res, "bf16", f"small {kind} B={B} C={C}")
+    compare_all(wl, g, lg, res, "bf16", f"small {kind} B={B} C={C}", inp.weights.w_lm)
     lay = res["layout"]
     if kind != "text":
         k, f = g.validate(torch.from_numpy(res["tokens"]).cuda())
@@ -98,7 +115,7 @@ def test_head_without_k_groups():
     shape = replace(SMALL, hidden=320)
     wl = small_workload("traj2d3d", 2, 64, seed=74, shape=shape, n_points=7, off_id=4099 - 1020 + 1002)
     inp, g, lg, res = run_both(wl)
-    compare_all(wl, g, lg, res, "bf16", "hidden 320")
+    compare_all(wl, g, lg, res, "bf16", "hidden 320", inp.weights.w_lm)
 
 
 def test_more_than_eight_split_partials():
@@ -109,7 +126,7 @@ def test_more_than_eight_split_partials():
     shape = replace(SMALL, inter=4096)
     wl = small_workload("text", 1, 64, seed=73, shape=shape, block_len=16)
     inp, g, lg, res = run_both(wl)
-    compare_all(wl, g, lg, res, "bf16", "16-way split-K sums")
+    compare_all(wl, g, lg, res, "bf16", "16-way split-K sums", inp.weights.w_lm)
 
 
 @pytest.mark.parametrize("n_layers", [1, 2, 3])
@@ -129,7 +146,7 @@ def test_tiny_fp32_workload():
     lg = g.argmax(logits=True)
     torch.cuda.synchronize()
     res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
-    compare_all(wl, g, lg, res, "f32", "tiny fp32")
+    compare_all(wl, g, lg, res, "f32", "tiny fp32", inp.weights.w_lm)
     k, f = g.validate()
     ko, fo = O.validate_primitive(g.toks.cpu().numpy(), res["layout"])
     assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
@@ -260,7 +277,7 @@ def test_full_size_workload(name):
     torch.cuda.synchronize()
     progress(f"[gpu] {name} done")
     res = oracle_result(name)
-    compare_all(wl, g, lg, res, "bf16", f"full {name}")
+    compare_all(wl, g, lg, res, "bf16", f"full {name}", inp.weights.w_lm)
     lay = res["layout"]
     if wl.schema["kind"] == "text":
         n = lay.L                  # every accepted length 0 .. L-1
@@ -276,8 +293,17 @@ def test_full_size_workload(name):
         ko, fo = O.validate_primitive(g.toks.cpu().numpy(), lay)
         assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
         if name == "traj2d3d":
-            n_off = int((g.toks.cpu().numpy() == lay.off_id).sum())
-            progress(f"[pairs] off-frame tokens {n_off} of {g.toks.numel()}")
+            # the pairing rule fires: some pairs go off-frame, and some need the
+            # joint decision (exactly one of the pair prefers OFF on its own)
+            t = g.toks.cpu().numpy()
+            n_off = int((t == lay.off_id).sum())
+            joint = 0
+            for (pu, pv) in lay.pairs:
+                own = [lay.legal(p)[int(np.argmax(res["logits"][0, p - 1, lay.legal(p)]))] == lay.off_id
+                       for p in (pu, pv)]
+                joint += own[0] != own[1]
+            progress(f"[pairs] off-frame tokens {n_off} of {t.size}; pairs decided jointly {joint}")
+            assert n_off >= 2 and joint >= 1
 
 
 def test_full_size_two_trajectory_blocks():
@@ -293,57 +319,62 @@ def test_full_size_two_trajectory_blocks():
     torch.cuda.synchronize()
     progress("[gpu] traj2d x2 done")
     res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
-    compare_all(wl, g, lg, res, "bf16", "full traj2d x2")
+    compare_all(wl, g, lg, res, "bf16", "full traj2d x2", inp.weights.w_lm)
     k, f = g.validate()
     ko, fo = O.validate_primitive(g.toks.cpu().numpy(), res["layout"])
     assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
 
 
-def test_full_size_points3d_sampled():
-    """B=8, L=2433, C=4096: the oracle cannot run the whole block in seconds,
-    so the sampled checks are: the LM head, argmax and validator on the GPU's
-    own hidden states for sampled rows, the context fusion for sampled
-    context rows, and legality of every token."""
+def test_full_size_points3d_requests_against_the_oracle():
+    """B = 8 independent requests, L = 2433, C = 4096 (M = 19,464 projection
+    rows: 128x256 tiles whose last row tile carries the 8 rows past 152 x 128,
+    for the QKV, O, gate/up and down projections).  The oracle runs requests 0
+    and 7 on their own (request 7 holds the carried rows): their context K/V,
+    hidden states, legal logits, tokens and acceptance are compared in full.
+    The LM head, argmax and validator are compared on all eight requests from
+    the GPU's own hidden states."""
     wl, inp = workload_inputs("points3d")
     g = GpuCase(wl, inp)
     g.fuse()
     g.draft()
-    g.argmax()
+    lg = g.argmax(logits=True)
     torch.cuda.synchronize()
-    m = O.Model(wl.shape, inp.weights)
+    progress("[gpu] points3d done")
     lay = O.build_layout(wl.schema, wl.shape.vocab)
-    hid = to_np(g.hidden)
-    assert np.all(np.isfinite(hid))
+    m = O.Model(wl.shape, inp.weights)
+    w_lm = inp.weights.w_lm
+    # every request: head stage on the GPU's hidden states, legality, validator
+    herr, hcnt = check_head_stage(g, lg, lay, w_lm, "bf16", "points3d")
     toks = g.toks.cpu().numpy()
-    rng = np.random.default_rng(5)
-    rows = rng.choice(wl.batch * (lay.L - 1), size=48, replace=False)
-    # sampled LM head: logits of the sampled rows from the GPU hidden states
-    H = wl.shape.hidden
-    hs = hid.reshape(-1, H)[rows]
-    lay_rows = [(int(r) // (lay.L - 1), int(r) % (lay.L - 1) + 1) for r in rows]
-    for (b, p), h in zip(lay_rows, hs):
-        ids = lay.legal(p)
-        z = inp.weights.w_lm[ids].astype(np.float64) @ h.astype(np.float64)
-        order = np.argsort(-z, kind="stable")
-        want = ids[order[0]]
-        gap = z[order[0]] - z[order[1]] if len(ids) > 1 else np.inf
-        if gap > 1e-2:
-            assert toks[b, p - 1] == want, (b, p)
-    for b in range(wl.batch):
-        for p in range(1, lay.L):
-            assert toks[b, p - 1] in lay.legal(p)
+    for p in range(1, lay.L):
+        assert np.isin(toks[:, p - 1], lay.legal(p)).all()
     k, f = g.validate()
     ko, fo = O.validate_primitive(toks, lay)
     assert np.array_equal(k.cpu().numpy(), ko) and np.array_equal(f.cpu().numpy(), fo)
-    # sampled context rows of the fusion
-    ck, cv = g.ctx_np()
-    samp = [(int(b), int(c)) for b, c in zip(rng.integers(0, wl.batch, 16), rng.integers(0, wl.ctx, 16))]
-    for (b, c) in samp:
-        sub = inp.feats[b:b + 1, :, c:c + 1, :]
-        kk, vv = O.fuse_context_kv(m, sub, ctx_pos0=c)
-        rel_close(ck[:, b, c], kk[:, 0, 0], "bf16", f"ctx_k row {b},{c}")
-        rel_close(cv[:, b, c], vv[:, 0, 0], "bf16", f"ctx_v row {b},{c}")
-    progress(f"[full points3d] valid requests {int((ko > 0).sum())} of {wl.batch}")
+    progress(f"[points3d head stage] logits row {herr[0]:.2e} elem {herr[1]:.2e}; tokens {hcnt}")
+    ck_all, cv_all = g.ctx_np()
+    hid_all = to_np(g.hidden)
+    lg_all = to_np(lg)
+    for b in (0, 7):
+        t = time.time()
+        ck, cv = O.fuse_context_kv(m, inp.feats[b:b + 1])
+        hid = O.draft_block(m, inp.tokens[b:b + 1], ck, cv)
+        zg = legal_logits(hid, w_lm, lay)
+        otoks = tokens_from_legal(zg, lay)
+        progress(f"[oracle] points3d request {b} in {time.time() - t:.1f}s")
+        e_k = rel_close(ck_all[:, b:b + 1], ck, "bf16", f"request {b} ctx_k")
+        e_v = rel_close(cv_all[:, b:b + 1], cv, "bf16", f"request {b} ctx_v")
+        e_h = rel_close(hid_all[b:b + 1], hid, "bf16", f"request {b} hidden")
+        e_z = rel_close_logits(lg_all[b:b + 1], zg, lay, "bf16", f"request {b} logits",
+                               scale=logit_scale(hid, w_lm, lay))
+        cnt = check_tokens_e2e(toks[b:b + 1], otoks, zg, lay, "bf16", f"request {b} tokens", gathered=True)
+        kb, fb = O.validate_primitive(otoks, lay)
+        if cnt[1] + cnt[2] == 0:   # identical tokens: identical acceptance
+            assert int(ko[b]) == int(kb[0]) and int(fo[b]) == int(fb[0])
+        progress(f"[parity points3d request {b}] ctx_k {e_k[0]:.2e}/{e_k[1]:.2e} ctx_v {e_v[0]:.2e}/{e_v[1]:.2e} "
+                 f"hidden {e_h[0]:.2e}/{e_h[1]:.2e} logits {e_z[0]:.2e}/{e_z[1]:.2e} (row/elem); "
+                 f"tokens agree/differ(gap>1e-2)/differ(gap<=1e-2) {cnt}; first_invalid gpu {int(fo[b])} "
+                 f"oracle {int(fb[0])}")
 
 
 def test_padding_memory_never_reaches_outputs():
@@ -369,7 +400,7 @@ def test_padding_memory_never_reaches_outputs():
     torch.cuda.synchronize()
     assert torch.isfinite(g.hidden.float()).all()
     res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
-    compare_all(wl, g, lg, res, "bf16", "NaN padding")
+    compare_all(wl, g, lg, res, "bf16", "NaN padding", inp.weights.w_lm)
 
 
 def test_validator_large_sets_from_global_memory():
@@ -426,7 +457,7 @@ def test_append_context_in_pieces_matches_one_fusion():
     lg = g.argmax(logits=True)
     torch.cuda.synchronize()
     res = O.run_block(O.Model(wl.shape, inp.weights), inp.feats, inp.tokens, wl.schema, want_logits=True)
-    compare_all(wl, g, lg, res, "bf16", "appended context")
+    compare_all(wl, g, lg, res, "bf16", "appended context", inp.weights.w_lm)
 
 
 def test_blocks_share_one_context():
@@ -435,6 +466,6 @@ def test_blocks_share_one_context():
     wl = small_workload("traj2d3d", 3, 77, seed=67, shared_ctx=True, n_points=5, off_id=4099 - 1020 + 1002)
     inp, g, lg, res = run_both(wl)
     assert g.ctx_k.shape[1] == 1
-    compare_all(wl, g, lg, res, "bf16", "shared context")
+    compare_all(wl, g, lg, res, "bf16", "shared context", inp.weights.w_lm)
     toks = res["tokens"]
     assert not np.array_equal(toks[0], toks[1])   # distinct anchors give distinct blocks

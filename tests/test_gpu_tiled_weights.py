@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("B,L,C,inter", [
     (1, 16, 64, 1408),     # 16 rows: split-K 32-row tiles
     (2, 25, 77, 1472),     # 50 rows; ragged MLP columns
-    (1, 129, 200, 1408),   # one leftover row carried by the last tile; context 200 rows
+    (1, 129, 200, 1408),   # 129 rows: the 128x256 tile split along K, a one-row last tile; context 200 rows
     (2, 100, 600, 1472),   # 200 rows (partly filled last tile); context 1200 rows
     (2, 150, 64, 1408),    # 300 rows: 128x128 8-wave tiles, K split (gate/up via the split-K sum)
 ])
@@ -31,7 +31,7 @@ def test_tiled_copies_match_row_major_bitwise(B, L, C, inter):
     shape = replace(SMALL, inter=inter)
     wl = small_workload("text", B, C, seed=90 + L, shape=shape, block_len=L)
     inp, g, lg, res = run_both(wl)
-    compare_all(wl, g, lg, res, "bf16", f"tiled weights B={B} L={L} C={C} I={inter}")
+    compare_all(wl, g, lg, res, "bf16", f"tiled weights B={B} L={L} C={C} I={inter}", inp.weights.w_lm)
     row = GpuCase(wl, inp, prepare=False)
     row.fuse()
     row.draft()
