@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -13,6 +14,11 @@
 #include "layout.h"
 
 using namespace fpd;
+
+// Static device scratch of fpd_draft_block_noalloc: 64 MiB per GPU, held
+// until the process ends (see noalloc_scratch below).
+static constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char g_noalloc_scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -531,6 +537,30 @@ int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32
   return FPD_OK;
 }
 
+// ---- the allocation-free entry point's scratch -----------------------------------
+// Device memory of fpd_draft_block_noalloc: one static array per GPU, held
+// until the process ends.  Host code never uses the array's name as an
+// address (in host code it is a stand-in): each device's address comes from
+// hipGetSymbolAddress with that device current, once, and is kept here.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int32_t noalloc_scratch(void** out) {
+  int dev = -1;
+  FPD_TRY_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FPD_E_UNSUPPORTED, "device index beyond 64");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    FPD_TRY_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_noalloc_scratch)));
+    if (!ptr) return fail(FPD_E_HIP, "hipGetSymbolAddress returned no address for the static scratch");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return FPD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -539,6 +569,23 @@ int32_t fpd_draft_block(const fpd_drafter* d, const int32_t* tokens, int32_t B, 
                         const void* ctx_v, int32_t C, int32_t ctx_cap, int32_t block_pos, void* hidden_out,
                         void* ws, size_t ws_bytes, void* stream) {
   return draft_impl(d, tokens, B, L, ctx_k, ctx_v, C, ctx_cap, block_pos, hidden_out, ws, ws_bytes, stream, false);
+}
+
+int32_t fpd_draft_block_noalloc(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L, const void* ctx_k,
+                                const void* ctx_v, int32_t C, int32_t ctx_cap, int32_t block_pos, void* hidden_out,
+                                void* stream) {
+  if (!d || !tokens || !hidden_out) return fail(FPD_E_ARG, "null argument");
+  if (B < 1 || L < 2 || C < 0 || block_pos < 0) return fail(FPD_E_SHAPE, "need B >= 1, L >= 2, C >= 0, block_pos >= 0");
+  if (too_many_rows(B, L) || too_many_rows(B, C)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
+  const size_t need = plan_draft(*d, B, L, C).total;
+  if (need > kNoallocScratchBytes)
+    return fail(FPD_E_WORKSPACE, "block needs " + std::to_string(need) + " bytes of scratch; the static scratch holds " +
+                                     std::to_string(kNoallocScratchBytes));
+  void* scratch_ptr = nullptr;
+  if (int32_t st = noalloc_scratch(&scratch_ptr)) return st;
+  NoTiming quiet;  // per-launch timing would create HIP events
+  return draft_impl(d, tokens, B, L, ctx_k, ctx_v, C, ctx_cap, block_pos, hidden_out, scratch_ptr,
+                    kNoallocScratchBytes, stream, false);
 }
 
 int32_t fpd_draft_blocks_shared_ctx(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32_t L,

@@ -23,6 +23,14 @@ class ProfScope {
   int idx_;
 };
 
+// While alive, the calling thread's launches record no timing (timing
+// creates HIP events, which the allocation-free entry point must not).
+class NoTiming {
+ public:
+  NoTiming();
+  ~NoTiming();
+};
+
 // ---- elementwise ------------------------------------------------------------
 hipError_t embed_gather(int dt, const int32_t* tokens, int M, const void* E, int H, int V, float* h,
                         hipStream_t st);

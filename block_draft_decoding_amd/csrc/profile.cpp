@@ -21,6 +21,7 @@ struct Rec {
 
 std::mutex g_mu;                  // guards the records and the event pool
 std::atomic<bool> g_on{false};    // read without the lock on every launch
+thread_local int t_quiet = 0;     // NoTiming scopes alive on this thread
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;  // events kept for reuse until the process ends
 
@@ -46,7 +47,7 @@ void recycle_all() {
 }  // namespace
 
 ProfScope::ProfScope(const char* tag, hipStream_t st) : st_(st), idx_(-1) {
-  if (!g_on.load(std::memory_order_relaxed)) return;
+  if (!g_on.load(std::memory_order_relaxed) || t_quiet > 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on.load(std::memory_order_relaxed)) return;
   Rec r{tag, take_event(), take_event()};
@@ -61,6 +62,9 @@ ProfScope::~ProfScope() {
   std::lock_guard<std::mutex> lk(g_mu);
   if (idx_ < (int)g_recs.size()) (void)hipEventRecord(g_recs[idx_].b, st_);
 }
+
+NoTiming::NoTiming() { ++t_quiet; }
+NoTiming::~NoTiming() { --t_quiet; }
 
 }  // namespace fpd
 

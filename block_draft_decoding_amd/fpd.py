@@ -89,6 +89,7 @@ _ws_size = _proto("fpd_workspace_size", [vp, i32, i32, i32, ctypes.POINTER(ctype
 _fuse = _proto("fpd_fuse_context_kv", [vp, vp, i32, i32, i32, vp, vp, i32, vp, ctypes.c_size_t, vp])
 _append = _proto("fpd_append_context_kv", [vp, vp, i32, i32, i32, vp, vp, i32, vp, ctypes.c_size_t, vp])
 _draft = _proto("fpd_draft_block", [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_size_t, vp])
+_draft_noalloc = _proto("fpd_draft_block_noalloc", [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp])
 _draft_shared = _proto("fpd_draft_blocks_shared_ctx", [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_size_t, vp])
 _argmax = _proto("fpd_constrained_argmax", [vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, vp])
 _validate = _proto("fpd_validate_primitive", [vp, vp, i32, vp, vp, vp])
@@ -352,6 +353,18 @@ def fpd_draft_block(d: Drafter, tokens: torch.Tensor, ctx_k: Optional[torch.Tens
                   _ptr(hidden_out, "hidden_out", d.dtype), _ptr(ws, "ws"), ws.numel(), _stream(stream)),
            "fpd_draft_block")
 
+
+
+def fpd_draft_block_noalloc(d: Drafter, tokens: torch.Tensor, ctx_k: Optional[torch.Tensor],
+                            ctx_v: Optional[torch.Tensor], C: int, hidden_out: torch.Tensor,
+                            block_pos: Optional[int] = None, stream=None) -> None:
+    """fpd_draft_block on the library's static scratch (no workspace)."""
+    B, L = tokens.shape
+    cap = ctx_k.shape[3] if ctx_k is not None else 0
+    _check(_draft_noalloc(d.handle, _ptr(tokens, "tokens", torch.int32), B, L, _ptr(ctx_k, "ctx_k", d.dtype),
+                          _ptr(ctx_v, "ctx_v", d.value_dtype), C, cap, C if block_pos is None else block_pos,
+                          _ptr(hidden_out, "hidden_out", d.dtype), _stream(stream)),
+           "fpd_draft_block_noalloc")
 
 
 def fpd_draft_blocks_shared_ctx(d: Drafter, tokens: torch.Tensor, ctx_k: torch.Tensor, ctx_v: torch.Tensor,

@@ -260,6 +260,21 @@ int32_t fpd_draft_block(const fpd_drafter *d, const int32_t *tokens, int32_t B, 
                         int32_t block_pos, void *hidden_out, void *ws, size_t ws_bytes,
                         void *stream);
 
+/* The same as fpd_draft_block without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Its scratch is a static
+ * 64 MiB device array inside the library, one per GPU, held until the process
+ * ends; nothing is allocated or freed, and no per-launch timing is recorded.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (no call needs it cleared), so calls that overlap on one GPU race:
+ * order them on one stream.  Errors as fpd_draft_block, plus FPD_E_WORKSPACE
+ * when the block needs more scratch than the array holds (fpd_workspace_size
+ * reports the need; the 64-waypoint 385-position block over 4,096 context
+ * rows takes about 47 MB), FPD_E_UNSUPPORTED beyond device index 63.       */
+int32_t fpd_draft_block_noalloc(const fpd_drafter *d, const int32_t *tokens, int32_t B, int32_t L,
+                                const void *ctx_k, const void *ctx_v, int32_t C, int32_t ctx_cap,
+                                int32_t block_pos, void *hidden_out, void *stream);
+
 /* Several primitives against one shared observation (VFlash paper,
  * conclusion and future work: complementary primitives predicted from one
  * observation).  Same as fpd_draft_block for B blocks of the same length L,
