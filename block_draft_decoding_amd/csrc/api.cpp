@@ -104,9 +104,12 @@ DraftWs plan_draft(const fpd_drafter& d, int B, int L, int C) {
   size_t pb = 0;
   pb = std::max(pb, gemm_partial_bytes(dt, m, (c.n_q + 2 * c.n_kv) * c.head_dim / 2, c.hidden,
                                        (c.n_q + 2 * c.n_kv) * c.head_dim, true));
-  pb = std::max(pb, gemm_partial_bytes(dt, m, c.hidden, qd, c.hidden, false));
-  pb = std::max(pb, gemm_partial_bytes(dt, m, c.inter, c.hidden, 2 * c.inter, true));
-  pb = std::max(pb, gemm_partial_bytes(dt, m, c.hidden, c.inter, c.hidden, false));
+  // O and the MLP run on all rows, and in the last layer of a single block on L - 1
+  for (const int mr : {m, B == 1 ? L - 1 : m}) {
+    pb = std::max(pb, gemm_partial_bytes(dt, mr, c.hidden, qd, c.hidden, false));
+    pb = std::max(pb, gemm_partial_bytes(dt, mr, c.inter, c.hidden, 2 * c.inter, true));
+    pb = std::max(pb, gemm_partial_bytes(dt, mr, c.hidden, c.inter, c.hidden, false));
+  }
   w.partial_bytes = pb;
   w.partial = take(pb);
   w.attn_bytes = attention_scratch_bytes(dt, B, L, C, c.n_q, c.n_kv, c.head_dim);
@@ -521,17 +524,28 @@ int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32
     at.ctx_bstride = shared_ctx ? 0 : 1;
     at.scale = (float)(1.0 / std::sqrt((double)dh));
     FPD_TRY_HIP(attention(dt, at, wsp(ws, w.attn), w.attn_bytes, s));
+    const bool last = li + 1 == c.n_layers;
+    // The last layer's output is read only at positions 1..L-1 (the anchor
+    // predicts nothing), so with one block its O projection and MLP run on
+    // those L-1 rows alone: the residual rows from row 1 on, the normed MLP
+    // input and SwiGLU output packed from row 0, the final norm written
+    // straight to hidden_out.  (The anchor's K/V, computed above, is still
+    // used by every query.)
+    const bool trim = last && B == 1;
+    const int Mr = trim ? L - 1 : M;
+    const size_t r0 = trim ? 1 : 0;
+    float* hr = h + r0 * H;
     // h += O W_o^T, a = RMSNorm(h) for the MLP
-    FPD_TRY_HIP(gemm_residual_norm(dt, at.o, M, qd, Wt{lw.w_o, tl ? d->t_o[li] : nullptr}, H, h, lw.g_mlp, c.rms_eps,
-                                   a, 0, part, w.partial_bytes, s, "gemm_o"));
+    FPD_TRY_HIP(gemm_residual_norm(dt, (const char*)at.o + r0 * qd * d->esz, Mr, qd,
+                                   Wt{lw.w_o, tl ? d->t_o[li] : nullptr}, H, hr, lw.g_mlp, c.rms_eps, a, 0, part,
+                                   w.partial_bytes, s, "gemm_o"));
     void* u = wsp(ws, w.u);
-    FPD_TRY_HIP(gemm_swiglu(dt, a, M, H, Wt{lw.w_gu, tl ? d->t_gu[li] : nullptr}, c.inter, u, part, w.partial_bytes,
+    FPD_TRY_HIP(gemm_swiglu(dt, a, Mr, H, Wt{lw.w_gu, tl ? d->t_gu[li] : nullptr}, c.inter, u, part, w.partial_bytes,
                             s));
     // h += u W_d^T, then the next layer's attention norm, or the final norm over positions 1..L-1
-    const bool last = li + 1 == c.n_layers;
-    FPD_TRY_HIP(gemm_residual_norm(dt, u, M, c.inter, Wt{lw.w_d, tl ? d->t_d[li] : nullptr}, H, h,
-                                   last ? d->w.g_final : d->layers[li + 1].g_attn,
-                                   c.rms_eps, last ? hidden_out : a, last ? L : 0, part, w.partial_bytes, s,
+    FPD_TRY_HIP(gemm_residual_norm(dt, u, Mr, c.inter, Wt{lw.w_d, tl ? d->t_d[li] : nullptr}, H, hr,
+                                   last ? d->w.g_final : d->layers[li + 1].g_attn, c.rms_eps,
+                                   last ? hidden_out : a, last && !trim ? L : 0, part, w.partial_bytes, s,
                                    "gemm_down"));
   }
   return FPD_OK;
