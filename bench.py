@@ -57,6 +57,45 @@ def kernel_work(tag, s, B, L, C, lay_info):
     return None
 
 
+def block_work(s, B, L, C, lay_info):
+    """Algorithmic (flops, bytes) of one drafted block: every layer's four
+    projections and attention over all B*L rows, plus the constrained LM
+    head; bytes are the weights read once, the context K/V and the legal
+    LM-head rows (activations are small next to them)."""
+    flops = 0.0
+    for tag in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention"):
+        flops += s.n_layers * kernel_work(tag, s, B, L, C, lay_info)[0]
+    flops += kernel_work("lm_head", s, B, L, C, lay_info)[0]
+    H, d, I = s.hidden, s.head_dim, s.inter
+    nqkv = (s.n_q + 2 * s.n_kv) * d
+    weights = s.n_layers * (nqkv * H + H * s.n_q * d + 2 * I * H + H * I) * 2
+    ctx_kv = s.n_layers * 2 * B * s.n_kv * C * d * 2
+    lm_rows = lay_info[1] * H * 2
+    return flops, weights + ctx_kv + lm_rows
+
+
+def host_description():
+    """CPU model and the BLAS numpy uses, for the CPU baseline."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy as np
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')} ({b.get('openblas configuration', '').strip()})"
+    except Exception:
+        pass
+    return model, blas
+
+
 def cpu_baseline(wl, inp, budget_s):
     """The oracle's warm block (layers, full-vocabulary logits, masked argmax,
     pairing, acceptance) on the host cores; context fusion done beforehand."""
@@ -89,7 +128,9 @@ def cpu_baseline(wl, inp, budget_s):
         times.append(time.time() - t)
     blk = statistics.median(times)
     tokens = wl.batch * (lay.L - 1)
+    model, blas = host_description()
     return {"value": tokens / blk, "unit": "drafted tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{len(times)} warm block(s) of the same workload (batch {wl.batch}, L={lay.L}, "
                       f"C={wl.ctx}), median {blk:.2f} s per block; context fusion {fuse_s:.2f} s not counted"}
 
@@ -267,6 +308,16 @@ def main():
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
     kernels = {t: {"launches_per_step": round(c[0] / nprof, 2), "ms_per_step": round(c[1] / nprof, 4)}
                for t, c in sorted(kern.items(), key=lambda kv: -kv[1][1])}
+    # the whole block against the chip: algorithmic work / measured step time
+    bflops, bbytes = block_work(s, B, L, C, (rows_cols, n_ids))
+    t_s = ms * 1e-3
+    block_roof = {"bound": "mfma" if bflops / bbytes >= RIDGE else "hbm",
+                  "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
+                  "achieved_tflops": round(bflops / t_s / 1e12, 2),
+                  "mfma_frac": round(bflops / t_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "achieved_gbs": round(bbytes / t_s / 1e9, 1),
+                  "hbm_frac": round(bbytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "roofline_ms": round(max(bflops / (PEAK_BF16_TFLOPS * 1e12), bbytes / (PEAK_HBM_GBS * 1e9)) * 1e3, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -296,6 +347,7 @@ def main():
         "cold_ms_per_step": round(fuse_ms + ms, 4),
         "accepted_k": k_out[:8].tolist(),
         "roofline": roof,
+        "block_roofline": block_roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

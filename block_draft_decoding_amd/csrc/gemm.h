@@ -15,16 +15,12 @@ namespace fpd {
 // Tile configurations of the bf16 GEMM: workgroup tile rows x columns, K
 // tile, wave grid (rows x columns of waves) and the depth of the
 // global -> LDS ring.  X(name, rows, cols, k_tile, waves_m, waves_n, stages).
-#define FPD_GEMM_CFGS(X)                      \
-  X(GEMM_128x128_S2, 128, 128, 64, 2, 2, 2)   \
-  X(GEMM_64x128_S3, 64, 128, 64, 2, 2, 3)     \
-  X(GEMM_32x128_S4, 32, 128, 64, 1, 2, 4)     \
-  X(GEMM_64x256_S3, 64, 256, 64, 1, 4, 3)     \
-  X(GEMM_128x256_W8_S2, 128, 256, 64, 2, 4, 2) \
-  X(GEMM_128x256_W8_S3, 128, 256, 64, 2, 4, 3) \
-  X(GEMM_256x128_W8_S3, 256, 128, 64, 4, 2, 3) \
-  X(GEMM_128x256_W8_K32_S5, 128, 256, 32, 2, 4, 5) \
-  X(GEMM_128x128_W8_S3, 128, 128, 64, 4, 2, 3)
+#define FPD_GEMM_CFGS(X)                          \
+  X(GEMM_32x128_S4, 32, 128, 64, 1, 2, 4)         \
+  X(GEMM_64x128_S3, 64, 128, 64, 2, 2, 3)         \
+  X(GEMM_128x128_W8_S3, 128, 128, 64, 4, 2, 3)    \
+  X(GEMM_128x256_W8_S3, 128, 256, 64, 2, 4, 3)    \
+  X(GEMM_256x256_W8_S2, 256, 256, 64, 2, 4, 2)
 enum GemmCfg {
 #define FPD_ENUM(name, ...) name,
   FPD_GEMM_CFGS(FPD_ENUM)
@@ -32,7 +28,7 @@ enum GemmCfg {
   GEMM_NUM_CFGS
 };
 struct GemmPlan {
-  int cfg = GEMM_128x128_S2;
+  int cfg = GEMM_128x256_W8_S3;
   int m_tiles = 1, n_tiles = 1, splits = 1;
   bool ext = false;           // the last row tile carries the rows past (m_tiles) * BM
   size_t partial_floats = 0;  // split-K scratch (splits * M * N_w floats) when splits > 1
@@ -52,7 +48,9 @@ int gemm_cfg_bk(int cfg);
 int gemm_cfg_extra_rows(int cfg, bool paired);
 // M rows, ncols logical output columns (pairs for paired epilogues), K depth,
 // nw = W rows covered (partial row length), paired = two W rows per column.
-GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired);
+// wide: 256x256 tiles may be chosen when they give two or more passes of
+// workgroups (off for the scattered q/k/v epilogue, which measured no gain).
+GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired, bool wide = true);
 
 // ---- K-tile-contiguous copies of the weights ----------------------------------
 // A projection's weights: row-major W [rows, K] (torch Linear layout) and,

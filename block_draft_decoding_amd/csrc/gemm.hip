@@ -771,8 +771,17 @@ GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int sp
 // that the row tiles (a partly filled last one counts its share of 32-row
 // blocks) cover about 80% of the CUs once; narrow plain outputs take 64x128 tiles
 // split along K.
-GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
+GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired, bool wide) {
   const int kt = K / 64;
+  // Many rows (the 8-request point-motion block, M = 19,464): 256x256 tiles
+  // move half the operand bytes per MFMA of 128x256 ones, which is what the
+  // per-CU operand fill rate bounds; with the last tile carrying up to 16
+  // leftover rows they took gate/up 1.93 -> 1.64 ms, down 1.21 -> 1.02 ms and
+  // O 0.61 -> 0.55 ms per launch there (q/k/v: no gain).
+  if (wide) {
+    const GemmPlan w256 = make_plan(GEMM_256x256_W8_S2, M, ncols, K, nw, paired, 1, /*fold=*/true);
+    if (w256.m_tiles * w256.n_tiles >= 512) return w256;
+  }
   auto with_splits = [&](int cfg, int lo, int hi) {
     GemmPlan p = make_plan(cfg, M, ncols, K, nw, paired, 1);
     const int tiles = p.m_tiles * p.n_tiles;
@@ -789,13 +798,16 @@ GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   // full row tile instead when that keeps the grid within one pass.
   if (folded.ext && big.m_tiles * big.n_tiles > 256 && folded.m_tiles * folded.n_tiles >= 224) return folded;
   if (big.m_tiles * big.n_tiles >= 224) return big;
-  if (M >= 256) {
+  const GemmPlan one = make_plan(GEMM_128x128_W8_S3, M, ncols, K, nw, paired, 1);
+  if (M >= 256 && one.m_tiles * one.n_tiles <= 256) {
     // Two or more full row tiles whose 128x256 tiles leave CUs idle (the QKV,
     // O and down projections of a few hundred rows): 128x128 tiles with 8
     // waves, K split as far as one pass of workgroups allows.  At M = 385 this
     // runs QKV unsplit (no separate split-K sum) and O / down 3-way split,
     // 7-8% faster than 128x256 tiles split 2-6 ways or 4-wave 64x128 tiles.
-    const GemmPlan one = make_plan(GEMM_128x128_W8_S3, M, ncols, K, nw, paired, 1);
+    // Where even unsplit 128x128 tiles would take a second pass (the fusion
+    // map over 2,048 context rows: 320 tiles), the 128x256 rules below are
+    // faster (fusion map 218 -> 182 us).
     const int s = std::max(1, std::min({8, 256 / (one.m_tiles * one.n_tiles), kt / 2}));
     return make_plan(GEMM_128x128_W8_S3, M, ncols, K, nw, paired, s);
   }
@@ -862,7 +874,7 @@ hipError_t gemm_qkv(int dt, const void* A, int M, int K, const Wt& Wqkv, const Q
   if (dt == FPD_DTYPE_BF16) {
     EpiQkv<bf16_t> e{(bf16_t*)o.q, (bf16_t*)o.k, (bf16_t*)o.vt, o.L, o.Lp, o.nq, o.nkv, o.d, half,
                      o.pos0, o.rope, o.tab};
-    GemmPlan pl = plan_gemm_bf16(M, pairs, K, nw, true);
+    GemmPlan pl = plan_gemm_bf16(M, pairs, K, nw, true, /*wide=*/false);
     if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) {
       pl.splits = 1;
       pl.partial_floats = 0;
