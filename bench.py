@@ -32,12 +32,26 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 BOX_TAU = 0.004             # confidence threshold of the box workloads' acceptance
 
 
-def kernel_work(tag, s, B, L, C, lay_info):
-    """Algorithmic (flops, bytes) of one launch of a kernel tag: what the
+TRIMMED = ("gemm_o", "gemm_gate_up", "gemm_down")
+
+
+def launch_rows(tag, s, B, L, layer):
+    """Rows one layer's launch of a kernel tag works on.  With one request the
+    last layer's O projection and MLP run on the L-1 rows whose hidden states
+    feed the LM head (the anchor row's output is never read)."""
+    if B == 1 and layer == s.n_layers - 1 and tag in TRIMMED:
+        return L - 1
+    return B * L
+
+
+def kernel_work(tag, s, B, L, C, lay_info, M=None):
+    """Algorithmic (flops, bytes) of one launch of a kernel tag on M rows
+    (default: the per-launch average over the block's layers): what the
     method must compute and move (weights once, activations in and out),
     without padding or re-reads."""
     H, nq, nkv, d, I = s.hidden, s.n_q, s.n_kv, s.head_dim, s.inter
-    M = B * L
+    if M is None:
+        M = sum(launch_rows(tag, s, B, L, i) for i in range(s.n_layers)) / s.n_layers
     e = 2  # bf16
     nqkv = (nq + 2 * nkv) * d
     if tag == "gemm_qkv":
@@ -59,12 +73,13 @@ def kernel_work(tag, s, B, L, C, lay_info):
 
 def block_work(s, B, L, C, lay_info):
     """Algorithmic (flops, bytes) of one drafted block: every layer's four
-    projections and attention over all B*L rows, plus the constrained LM
-    head; bytes are the weights read once, the context K/V and the legal
+    projections and attention over the rows launch_rows gives, plus the
+    constrained LM head; bytes are the weights read once, the context K/V and the legal
     LM-head rows (activations are small next to them)."""
     flops = 0.0
     for tag in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention"):
-        flops += s.n_layers * kernel_work(tag, s, B, L, C, lay_info)[0]
+        for i in range(s.n_layers):
+            flops += kernel_work(tag, s, B, L, C, lay_info, M=launch_rows(tag, s, B, L, i))[0]
     flops += kernel_work("lm_head", s, B, L, C, lay_info)[0]
     H, d, I = s.hidden, s.head_dim, s.inter
     nqkv = (s.n_q + 2 * s.n_kv) * d
