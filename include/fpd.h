@@ -30,17 +30,23 @@
  *   - Weight tensors are BORROWED: the drafter keeps the device pointers,
  *     copies nothing, and the caller keeps the memory alive and unchanged
  *     until fpd_drafter_destroy.  W_lm may alias the embedding.
- *   - The calls that take a `stream` (a hipStream_t passed as void*, NULL =
- *     the default stream) only enqueue work: they never allocate, never
- *     synchronise and return as soon as the work is queued.  The caller
- *     synchronises before reading results.
+ *   - The hot-path calls, which take a `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream), only enqueue work: they never
+ *     allocate, never synchronise and return as soon as the work is
+ *     queued.  The caller synchronises before reading results.
  *   - Arguments are checked on the host before anything is enqueued: a
  *     non-zero status means nothing was written.  FPD_E_HIP reports a
  *     launch failure (text in fpd_last_error); work enqueued before the
  *     failure may have run.
- *   - Handles are immutable after creation; calls on different streams
- *     with distinct workspaces may run concurrently.  Calls sharing a
- *     workspace must be ordered on one stream.
+ *   - Handles are immutable after set-up: a drafter may be changed only by
+ *     fpd_drafter_prepare, which the caller makes once, before any other
+ *     call uses the drafter and from one thread.  After that, calls on
+ *     different streams with distinct workspaces may run concurrently.
+ *     Calls sharing a workspace must be ordered on one stream.
+ *   - The hot-path calls touch no global state except an atomic flag that
+ *     says whether per-launch timing (fpd_profile_enable) is on (with it
+ *     off they take no lock) and, for fpd_draft_block_noalloc, the table
+ *     of each device's static scratch address (read under a lock).
  *   - fpd_last_error() is thread-local and describes the most recent
  *     failing call on the calling thread.
  */
@@ -171,6 +177,8 @@ int32_t fpd_drafter_destroy(fpd_drafter *d);
  * another, so each K step of a GEMM workgroup reads 4 KB-contiguous runs
  * of weights instead of 128-byte pieces of rows that lie 2 K bytes apart.
  * Later calls read the copies (same results: only the addresses change).
+ * Call it once, right after fpd_drafter_create and before any other call
+ * uses the drafter: it changes the handle, so it must not race with them.
  * The row-major weights stay borrowed (embed, w_lm and the norms are read
  * from them).  No-op for F32 drafters and for a drafter already prepared.
  * Allocating; synchronises `stream` (a hipStream_t, NULL = default).
