@@ -19,8 +19,14 @@
 // The key range
 // is split across workgroups when (b, kv-head, query-tile) alone cannot fill
 // the GPU; partial (m, l, O) (O as per-row-scaled fp16) are merged by a
-// log-sum-exp combine.
+// log-sum-exp combine.  When the packed rows end in a tile of at most 32
+// rows (L = 64k + 1 leaves 4), that tail tile runs in workgroups of its own
+// where two waves share every key tile (keys 0-31 / 32-63) and merge their
+// states at the end: a wave alone per SIMD, each doing half the work of a
+// full tile's wave, so the tail takes fewer key splits and frees CUs for
+// more splits of the full tiles.
 #include <algorithm>
+#include <type_traits>
 
 #include "../../include/fpd.h"
 #include "kernels.h"
@@ -33,7 +39,8 @@ constexpr int KT = 64;          // keys per tile
 constexpr int D = 128;          // head dim of the bf16 path
 constexpr int AW = 8;           // waves per workgroup
 constexpr int QROWS = AW * 32;  // packed query rows per workgroup
-constexpr int AST = 3;          // depth of the global -> LDS ring
+constexpr int AST = 3;          // depth of the global -> LDS ring (8-wave query tiles)
+constexpr int TST = 5;          // depth of the ring of the tail tile's workgroups
 constexpr int KSLOTS = KT * 16; // 16-byte chunks of a K tile (64 keys x 256 bytes)
 constexpr int VSLOTS = D * 8;   // 16-byte chunks of a V^T tile (128 dims x 64 keys)
 constexpr int ASTAGE = KSLOTS + VSLOTS;
@@ -60,7 +67,10 @@ struct AttnP {
   bf16_t* o;
   uint16_t* opart;  // [splits, B, nq, L, D] fp16: each split's O / (l c), c = its row's max |O / l|
   float* mlpart;    // [splits, B, nq, L, 4]: reference max (log2 units), l, c, unused
-  int B, L, Lp, C, cap, nq, nkv, g, R, q_tiles, splits, ctx_tiles, blk_tiles, ctx_bstride;
+  int B, L, Lp, C, cap, nq, nkv, g, R, ctx_tiles, blk_tiles, ctx_bstride;
+  int q_tiles;      // query tiles of 8-wave workgroups per (b, kv head)
+  int splits;       // their key splits = partial slots per row
+  int tail_splits;  // key splits of the tail tile (after the q_tiles), 0 = none
   float scale_log2;
 };
 
@@ -79,19 +89,33 @@ __device__ __forceinline__ int vslot(int d, int c) { return d * 8 + (c ^ ((d >> 
 // partial tiles of a workgroup their V^T columns are zeroed in LDS before
 // use, so padding memory never reaches the P V product.
 __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
-  __shared__ u32x4_t lds[AST * ASTAGE];
+  __shared__ u32x4_t lds[(AST > TST ? AST : TST) * ASTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = tile % p.q_tiles;
-  const int rest = tile / p.q_tiles;
-  const int sp = rest % p.splits;
-  const int bh = rest / p.splits;
+  // Each (b, kv head) owns a contiguous range of tiles: its (query tile,
+  // split) pairs of the 8-wave query tiles, query tile fastest, then the
+  // splits of the tail tile, whose rows waves 0 and 1 both hold (each takes
+  // one 32-key half of every key tile).  A range of tiles runs on one XCD,
+  // so all the workgroups that stream one head's keys share its L2.
+  const int per_bh = p.q_tiles * p.splits + p.tail_splits;
+  const int bh = tile / per_bh, local = tile % per_bh;
+  const bool tail = local >= p.q_tiles * p.splits;
+  int qt, sp, ns;
+  if (!tail) {
+    qt = local % p.q_tiles;
+    sp = local / p.q_tiles;
+    ns = p.splits;
+  } else {
+    qt = p.q_tiles;
+    sp = local - p.q_tiles * p.splits;
+    ns = p.tail_splits;
+  }
   const int b = bh / p.nkv, j = bh % p.nkv;
   const int lq = lane & 31, lg = lane >> 5;
-  const int r0 = qt * QROWS + wave * 32;
-  const bool wave_active = r0 < p.R;
+  const int r0 = qt * QROWS + (tail ? 0 : wave * 32);
+  const bool wave_active = tail ? wave < 2 : r0 < p.R;
   const int qrow = r0 + lq;
   const bool qvalid = qrow < p.R;
 
@@ -103,7 +127,7 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
     qf[kk] = qvalid ? *(const bf16x8_t*)(qbase + (size_t)qrow * D + kk * 16 + lg * 8) : bf16x8_t{};
 
   const int total = p.ctx_tiles + p.blk_tiles;
-  const int t0 = (int)((long)sp * total / p.splits), t1 = (int)((long)(sp + 1) * total / p.splits);
+  const int t0 = (int)((long)sp * total / ns), t1 = (int)((long)(sp + 1) * total / ns);
   const size_t bhk = (size_t)b * p.nkv + j;
   const size_t cbhk = (size_t)b * p.ctx_bstride * p.nkv + j;  // context segment (shared: b = 0)
 
@@ -148,105 +172,162 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
   float m_run = -INFINITY, l_run = 0.f;
   const int krow0 = swap23(lq);
 
+  // The key loop over an ST-deep ring; a wave works on NKB 32-key blocks of
+  // each tile starting at block kb0 (NKB = 2, kb0 = 0 in the 8-wave tiles;
+  // NKB = 1, kb0 = wave in the tail tile, whose workgroup streams twice the
+  // keys of a full tile's and so keeps more tiles in flight).
+  auto run = [&](auto nkb_c, auto st_c, int kb0) {
+    constexpr int NKB = decltype(nkb_c)::value;
+    constexpr int ST = decltype(st_c)::value;
 #pragma unroll
-  for (int s2 = 0; s2 < AST - 1; ++s2)
-    if (t0 + s2 < t1) issue(t0 + s2, s2);
-  wait_lgkm0();
+    for (int s2 = 0; s2 < ST - 1; ++s2)
+      if (t0 + s2 < t1) issue(t0 + s2, s2);
+    wait_lgkm0();
 
-  for (int t = t0; t < t1; ++t) {
-    const int stage = (t - t0) % AST;
-    const int key0 = tile_key0(t), count = tile_count(t);
-    wait_stages<2 * APT, AST - 2>(min(AST - 2, t1 - 1 - t));
-    barrier_nofence();  // tile t landed for every wave; stage of tile t-1 is free
-    u32x4_t* Ks = lds + stage * ASTAGE;
-    u32x4_t* Vs = Ks + KSLOTS;
-    if (key0 + KT > count) {  // partial tile: zero the V^T columns of keys past the count
-      for (int sl = tid; sl < VSLOTS; sl += AW * 64) {
-        const int dr = sl >> 3, c = (sl & 7) ^ ((dr >> 1) & 7);
-        const int nvalid = count - (key0 + c * 8);
-        if (nvalid < 8) {
-          u32x4_t v = Vs[sl];
+    for (int t = t0; t < t1; ++t) {
+      const int stage = (t - t0) % ST;
+      const int key0 = tile_key0(t), count = tile_count(t);
+      wait_stages<2 * APT, ST - 2>(min(ST - 2, t1 - 1 - t));
+      barrier_nofence();  // tile t landed for every wave; stage of tile t-1 is free
+      u32x4_t* Ks = lds + stage * ASTAGE;
+      u32x4_t* Vs = Ks + KSLOTS;
+      if (key0 + KT > count) {  // partial tile: zero the V^T columns of keys past the count
+        for (int sl = tid; sl < VSLOTS; sl += AW * 64) {
+          const int dr = sl >> 3, c = (sl & 7) ^ ((dr >> 1) & 7);
+          const int nvalid = count - (key0 + c * 8);
+          if (nvalid < 8) {
+            u32x4_t v = Vs[sl];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (2 * e >= nvalid) v[e] = 0;
-            else if (2 * e + 1 >= nvalid) v[e] &= 0xffffu;
+            for (int e = 0; e < 4; ++e) {
+              if (2 * e >= nvalid) v[e] = 0;
+              else if (2 * e + 1 >= nvalid) v[e] &= 0xffffu;
+            }
+            Vs[sl] = v;
           }
-          Vs[sl] = v;
         }
+        wait_lgkm0();
+        barrier_nofence();
       }
-      wait_lgkm0();
-      barrier_nofence();
-    }
-    if (t + AST - 1 < t1) issue(t + AST - 1, (t - t0 + AST - 1) % AST);
-    if (wave_active) {
-      const bf16x8_t* Kb = (const bf16x8_t*)Ks;
-      const f16x8_t* Vh = (const f16x8_t*)Vs;
-      f32x16_t s[2];
+      if (t + ST - 1 < t1) issue(t + ST - 1, (t - t0 + ST - 1) % ST);
+      if (wave_active) {
+        const bf16x8_t* Kb = (const bf16x8_t*)Ks;
+        const f16x8_t* Vh = (const f16x8_t*)Vs;
+        f32x16_t s[NKB];
+        if constexpr (NKB == 2) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+          for (int i = 0; i < NKB; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const int krow = kb * 32 + krow0;
+            for (int r = 0; r < 16; ++r) s[i][r] = 0.f;
+            const int krow = (kb0 + i) * 32 + krow0;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[kslot(krow, kk * 2 + lg)], qf[kk], s[kb], 0, 0, 0);
-      }
-      // register r of sub-block kb holds key kb*32 + (r/8)*16 + lg*8 + r%8 for query lq.
-      // The running max is kept in raw score units (scale > 0); exponents
-      // are fma(s, scale*log2(e), -m*scale*log2(e)).
-      float mloc = -INFINITY;
-      if (key0 + KT <= count) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kb][r]);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r >> 3) * 16 + lg * 8 + (r & 7);
-            s[kb][r] = key < count ? s[kb][r] : -INFINITY;
-            mloc = fmaxf(mloc, s[kb][r]);
+            for (int kk = 0; kk < D / 16; ++kk)
+              s[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[kslot(krow, kk * 2 + lg)], qf[kk], s[i], 0, 0, 0);
           }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      // keep the reference max unless it would let exponents exceed 2^kRescale
-      const bool grow = (mloc - m_run) * p.scale_log2 > kRescale;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mloc : m_run;
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2) : 1.0f;
-        l_run *= alpha;
+        } else {
+          // one key block: two accumulator chains (even / odd head-dim
+          // steps) so that consecutive MFMAs do not wait on each other
+          f32x16_t s2;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+          for (int r = 0; r < 16; ++r) s[0][r] = s2[r] = 0.f;
+          const int krow = kb0 * 32 + krow0;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run * p.scale_log2;
+          for (int kk = 0; kk < D / 16; kk += 2) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[kslot(krow, kk * 2 + lg)], qf[kk], s[0], 0, 0, 0);
+            s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[kslot(krow, kk * 2 + 2 + lg)], qf[kk + 1], s2, 0, 0, 0);
+          }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, neg_m));
-          s[kb][r] = e;
-          l_run += e;
+          for (int r = 0; r < 16; ++r) s[0][r] += s2[r];
         }
-      // P in fp16 (values in [0, 2^kRescale]; 11 significant bits) against
-      // the fp16 values, which hold the bf16-rounded V exactly
+        // register r of block kb holds key kb*32 + (r/8)*16 + lg*8 + r%8 for query lq.
+        // The running max is kept in raw score units (scale > 0); exponents
+        // are fma(s, scale*log2(e), -m*scale*log2(e)).
+        float mloc = -INFINITY;
+        if (key0 + KT <= count) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int i = 0; i < NKB; ++i)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f16x8_t pf;
+            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[i][r]);
+        } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (_Float16)s[kb][h * 8 + e];
+          for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = key0 + (kb0 + i) * 32 + (r >> 3) * 16 + lg * 8 + (r & 7);
+              s[i][r] = key < count ? s[i][r] : -INFINITY;
+              mloc = fmaxf(mloc, s[i][r]);
+            }
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        // keep the reference max unless it would let exponents exceed 2^kRescale
+        const bool grow = (mloc - m_run) * p.scale_log2 > kRescale;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mloc : m_run;
+          const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2) : 1.0f;
+          l_run *= alpha;
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Vh[vslot(dt * 32 + lq, kb * 4 + h * 2 + lg)], pf,
-                                                           o[dt], 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+          m_run = m_new;
         }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run * p.scale_log2;
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[i][r], p.scale_log2, neg_m));
+            s[i][r] = e;
+            l_run += e;
+          }
+        // P in fp16 (values in [0, 2^kRescale]; 11 significant bits) against
+        // the fp16 values, which hold the bf16-rounded V exactly
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            f16x8_t pf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[e] = (_Float16)s[i][h * 8 + e];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Vh[vslot(dt * 32 + lq, (kb0 + i) * 4 + h * 2 + lg)],
+                                                             pf, o[dt], 0, 0, 0);
+          }
+      }
     }
+  };
+  if (tail)
+    run(std::integral_constant<int, 1>{}, std::integral_constant<int, TST>{}, wave & 1);
+  else
+    run(std::integral_constant<int, 2>{}, std::integral_constant<int, AST>{}, 0);
+
+  if (tail) {
+    // Wave 1 hands its (m, l, O) for the other half of the keys to wave 0
+    // through a ring stage that no wave reads any more (the last tile used
+    // stage (n - 1) % TST, and every wave has passed the barrier that ended
+    // the tile before it).
+    float* xch = (float*)(lds + ((t1 - t0) % TST) * ASTAGE);
+    if (wave == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(dt * 16 + r) * 64 + lane] = o[dt][r];
+      xch[64 * 64 + lane] = m_run;
+      xch[65 * 64 + lane] = l_run;
+    }
+    wait_lgkm0();
+    barrier_nofence();
+    if (wave != 0) return;
+    const float m1 = xch[64 * 64 + lane], l1 = xch[65 * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mm) * p.scale_log2);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * p.scale_log2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * a0 + xch[(dt * 16 + r) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = mm;
   }
 
   if (!qvalid) return;
@@ -290,7 +371,15 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
         w[1] = pack_f16x2(o[dt][q4 * 4 + 2] * inv, o[dt][q4 * 4 + 3] * inv);
         *(u32x2_t*)(dst + d0) = w;
       }
-    if (lg == 0) *(f32x4_t*)(p.mlpart + row * 4) = f32x4_t{m_run * p.scale_log2, l_tot, c, 0.f};
+    if (lg == 0) {
+      *(f32x4_t*)(p.mlpart + row * 4) = f32x4_t{m_run * p.scale_log2, l_tot, c, 0.f};
+      // the tail tile fills fewer slots: its first split marks the rest empty
+      if (tail && sp == 0) {
+        const size_t rows = (size_t)p.B * p.nq * p.L;
+        for (int s2 = ns; s2 < p.splits; ++s2)
+          *(f32x4_t*)(p.mlpart + (row + s2 * rows) * 4) = f32x4_t{-INFINITY, 0.f, 1.f, 0.f};
+      }
+    }
   }
 }
 
@@ -410,7 +499,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   }
 }
 
-int attn_splits(int B, int L, int C, int nq, int nkv, int* q_tiles_out, int* total_tiles) {
+// Work split of the bf16 attention.
+struct AttnPlan {
+  int q_tiles = 1;      // 8-wave query tiles per (b, kv head)
+  int splits = 1;       // their key splits = partial slots per row
+  int tail_splits = 0;  // key splits of the tail tile, 0 = no tail tile
+};
+
+AttnPlan attn_plan(int B, int L, int C, int nq, int nkv) {
   const int g = nq / nkv;
   const int R = g * L;
   const int q_tiles = (R + QROWS - 1) / QROWS;
@@ -420,18 +516,33 @@ int attn_splits(int B, int L, int C, int nq, int nkv, int* q_tiles_out, int* tot
   // pass over the 256 CUs (more splits only add combine traffic), keeping at
   // least two key tiles per split (one-tile splits write a partial O per
   // tile: slower on short blocks over 2,048 keys, measured)
-  int splits = 1;
-  while (base * splits * 2 <= 256 && splits * 2 * 2 <= tiles && splits < 32) splits *= 2;
-  if (q_tiles_out) *q_tiles_out = q_tiles;
-  if (total_tiles) *total_tiles = tiles;
-  return splits;
+  AttnPlan pl;
+  pl.q_tiles = q_tiles;
+  while (base * pl.splits * 2 <= 256 && pl.splits * 2 * 2 <= tiles && pl.splits < 32) pl.splits *= 2;
+  // A last tile of at most 32 rows (one busy wave) goes to tail workgroups
+  // with two key splits, whose two waves (one per SIMD) each take half of
+  // every key tile; the full tiles then split as far as the pass allows.
+  // Up to 7 splits the tail's 2 * 850-cycle half tiles finish before the
+  // full tiles' 3,300-cycle tiles (two waves per SIMD).
+  const int rt = R - (q_tiles - 1) * QROWS;
+  if (q_tiles >= 2 && rt <= 32) {
+    const int nf = (q_tiles - 1) * B * nkv, nt = B * nkv, ts = 2;
+    int s = (256 - nt * ts) / nf;
+    s = std::min(s, std::min(tiles / 2, 7));
+    if (s > pl.splits && s >= ts) {
+      pl.q_tiles = q_tiles - 1;
+      pl.splits = s;
+      pl.tail_splits = ts;
+    }
+  }
+  return pl;
 }
 
 }  // namespace
 
 size_t attention_scratch_bytes(int dt, int B, int L, int C, int nq, int nkv, int d) {
   if (dt != FPD_DTYPE_BF16) return 0;
-  const int s = attn_splits(B, L, C, nq, nkv, nullptr, nullptr);
+  const int s = attn_plan(B, L, C, nq, nkv).splits;
   if (s == 1) return 0;
   const size_t rows = (size_t)s * B * nq * L;
   return rows * d * sizeof(uint16_t) + rows * 4 * sizeof(float);
@@ -450,16 +561,23 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
     p.ctx_bstride = a.ctx_bstride;
     p.g = a.nq / a.nkv;
     p.R = p.g * a.L;
-    int total = 0;
-    p.splits = attn_splits(a.B, a.L, a.C, a.nq, a.nkv, &p.q_tiles, &total);
+    const AttnPlan pl = attn_plan(a.B, a.L, a.C, a.nq, a.nkv);
+    p.q_tiles = pl.q_tiles;
+    p.splits = pl.splits;
+    p.tail_splits = pl.tail_splits;
     const size_t rows = (size_t)p.splits * a.B * a.nq * a.L;
-    if (p.splits > 1 && rows * (D * sizeof(uint16_t) + 4 * sizeof(float)) > scratch_bytes) p.splits = 1;
+    if (p.splits > 1 && rows * (D * sizeof(uint16_t) + 4 * sizeof(float)) > scratch_bytes) {
+      // no room for the partials: one workgroup per query tile covers every key
+      p.q_tiles = (p.R + QROWS - 1) / QROWS;
+      p.splits = 1;
+      p.tail_splits = 0;
+    }
     p.ctx_tiles = (a.C + KT - 1) / KT;
     p.blk_tiles = (a.L + KT - 1) / KT;
     p.opart = (uint16_t*)scratch;
     p.mlpart = (float*)((uint16_t*)scratch + rows * D);
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    const int grid = p.q_tiles * p.splits * a.B * a.nkv;
+    const int grid = (p.q_tiles * p.splits + p.tail_splits) * a.B * a.nkv;
     {
       ProfScope prof("attention", st);
       hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(AW * 64), 0, st, p);
@@ -476,7 +594,11 @@ hipError_t attention(int dt, const AttnArgs& a, void* scratch, size_t scratch_by
                        (bf16_t*)a.o);                                                                          \
     break;
       FPD_COMB(2)
+      FPD_COMB(3)
       FPD_COMB(4)
+      FPD_COMB(5)
+      FPD_COMB(6)
+      FPD_COMB(7)
       FPD_COMB(8)
       FPD_COMB(16)
       FPD_COMB(32)

@@ -109,6 +109,17 @@ def test_small_bf16_end_to_end(kind, B, C, over):
         progress(f"[pairs] off-frame tokens {n_off} of {res['tokens'].size}")
 
 
+# 4L packed rows per KV head (n_q = 8, n_kv = 2): L = 65 and 72 end in a
+# tail tile of 4 and 32 rows, which runs in its own two-split workgroups
+# while the full tile takes 3 (C = 300) or 7 (C = 1000) key splits; L = 73
+# leaves 36 rows, more than one wave holds, and keeps the plain plan.
+@pytest.mark.parametrize("B,C,L", [(2, 300, 65), (1, 1000, 72), (2, 300, 73)])
+def test_tail_query_tile(B, C, L):
+    wl = small_workload("text", B, C, seed=80 + L, block_len=L)
+    inp, g, lg, res = run_both(wl)
+    compare_all(wl, g, lg, res, "bf16", f"tail tile B={B} C={C} L={L}", inp.weights.w_lm)
+
+
 def test_head_without_k_groups():
     """Hidden 320 = 5 K tiles: the narrow-chunk LM head cannot split K into
     wave groups and runs one wave per item."""
