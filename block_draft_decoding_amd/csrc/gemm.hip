@@ -43,14 +43,26 @@ struct MapGlu {    // pair index i -> (i, I + i)
 };
 
 // ---- epilogues --------------------------------------------------------------
+// Plain epilogues store (EpiStore) or add into (EpiResid, kRmw) an f32
+// matrix.  Paired epilogues split into col(p), the per-column state a lane
+// computes once for the column pairs it holds, and pair(m, col, x0, x1) per
+// row, so that nothing per column is re-read after the stores of earlier
+// rows (a lane-indexed kernel-argument table would otherwise be re-loaded,
+// one memory round trip per output pair).
 struct EpiStore {
+  static constexpr bool kRmw = false;
   float* out;
   int ld;
-  __device__ void operator()(int m, int n, float v) const { out[(size_t)m * ld + n] = v; }
+  __device__ float load(int, int) const { return 0.f; }
+  __device__ void store(int m, int n, float v) const { out[(size_t)m * ld + n] = v; }
+  __device__ void operator()(int m, int n, float v) const { store(m, n, v); }
 };
 struct EpiResid {
+  static constexpr bool kRmw = true;
   float* h;
   int ld;
+  __device__ float load(int m, int n) const { return h[(size_t)m * ld + n]; }
+  __device__ void store(int m, int n, float v) const { h[(size_t)m * ld + n] = v; }
   __device__ void operator()(int m, int n, float v) const { h[(size_t)m * ld + n] += v; }
 };
 
@@ -59,21 +71,29 @@ struct EpiQkv {
   T *q, *k, *vt;
   int L, Lp, nq, nkv, d, half, pos0, rope;
   RopeTab tab;
-  __device__ void pair(int m, int p, float x0, float x1) const {
-    const int head = p / half, i = p % half;
+  struct Col {
+    int head, i;
+    double inv_rev;
+  };
+  __device__ Col col(int p) const {
+    const int i = p % half;
+    return Col{p / half, i, tab.inv_rev[i]};
+  }
+  __device__ void pair(int m, const Col& c, float x0, float x1) const {
     const int b = m / L, l = m - b * L;
-    if (head < nq + nkv) {
-      if (rope) rope_pair(x0, x1, pos0 + l, tab.inv_rev[i]);
-      T* dst = head < nq ? q + (((size_t)b * nq + head) * L + l) * d
-                         : k + (((size_t)b * nkv + (head - nq)) * L + l) * d;
-      Elem<T>::st(dst + i, x0);
-      Elem<T>::st(dst + i + half, x1);
+    if (c.head < nq + nkv) {
+      if (rope) rope_pair(x0, x1, pos0 + l, c.inv_rev);
+      T* dst = c.head < nq ? q + (((size_t)b * nq + c.head) * L + l) * d
+                           : k + (((size_t)b * nkv + (c.head - nq)) * L + l) * d;
+      Elem<T>::st(dst + c.i, x0);
+      Elem<T>::st(dst + c.i + half, x1);
     } else {
-      T* dst = vt + ((size_t)b * nkv + (head - nq - nkv)) * d * Lp + l;
-      ValueStore<T>::st(dst + (size_t)i * Lp, x0);
-      ValueStore<T>::st(dst + (size_t)(i + half) * Lp, x1);
+      T* dst = vt + ((size_t)b * nkv + (c.head - nq - nkv)) * d * Lp + l;
+      ValueStore<T>::st(dst + (size_t)c.i * Lp, x0);
+      ValueStore<T>::st(dst + (size_t)(c.i + half) * Lp, x1);
     }
   }
+  __device__ void pair(int m, int p, float x0, float x1) const { pair(m, col(p), x0, x1); }
 };
 
 template <class T>
@@ -81,26 +101,36 @@ struct EpiCtx {
   T *k, *vt;
   int C, cap, nkv, d, half, pos0, rope;
   RopeTab tab;
-  __device__ void pair(int m, int p, float x0, float x1) const {
-    const int head = p / half, i = p % half;
+  struct Col {
+    int head, i;
+    double inv_rev;
+  };
+  __device__ Col col(int p) const {
+    const int i = p % half;
+    return Col{p / half, i, tab.inv_rev[i]};
+  }
+  __device__ void pair(int m, const Col& cc, float x0, float x1) const {
     const int b = m / C, c = m - b * C;
-    if (head < nkv) {
-      if (rope) rope_pair(x0, x1, pos0 + c, tab.inv_rev[i]);
-      T* dst = k + (((size_t)b * nkv + head) * cap + c) * d;
-      Elem<T>::st(dst + i, x0);
-      Elem<T>::st(dst + i + half, x1);
+    if (cc.head < nkv) {
+      if (rope) rope_pair(x0, x1, pos0 + c, cc.inv_rev);
+      T* dst = k + (((size_t)b * nkv + cc.head) * cap + c) * d;
+      Elem<T>::st(dst + cc.i, x0);
+      Elem<T>::st(dst + cc.i + half, x1);
     } else {
-      T* dst = vt + ((size_t)b * nkv + (head - nkv)) * d * cap + c;
-      ValueStore<T>::st(dst + (size_t)i * cap, x0);
-      ValueStore<T>::st(dst + (size_t)(i + half) * cap, x1);
+      T* dst = vt + ((size_t)b * nkv + (cc.head - nkv)) * d * cap + c;
+      ValueStore<T>::st(dst + (size_t)cc.i * cap, x0);
+      ValueStore<T>::st(dst + (size_t)(cc.i + half) * cap, x1);
     }
   }
+  __device__ void pair(int m, int p, float x0, float x1) const { pair(m, col(p), x0, x1); }
 };
 
 template <class T>
 struct EpiGlu {
   T* u;
   int I;
+  using Col = int;
+  __device__ Col col(int p) const { return p; }
   __device__ void pair(int m, int p, float g, float up) const {
     Elem<T>::st(u + (size_t)m * I + p, silu_f(g) * up);
   }
@@ -397,60 +427,127 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   if constexpr (XR > 0) {
     // extra rows (16x16 blocks): lane holds column lane % 16, rows 4 (lane / 16) + r
     if (ext) {
+      if (part) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + BM + 4 * (lane >> 4) + r;
-        if (m >= M) continue;
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + BM + 4 * (lane >> 4) + r;
+          if (m >= M) continue;
 #pragma unroll
-        for (int b = 0; b < XB; ++b) {
-          const int c = c0 + xcol0 + 16 * b + (lane & 15);
-          if (c >= ncols) continue;
-          if constexpr (PAIRED) {
-            const float v0 = xacc[b][r], v1 = xacc[XB + b][r];
-            if (part) {
-              part[(size_t)m * part_ld + map.first(c)] = v0;
-              part[(size_t)m * part_ld + map.second(c)] = v1;
+          for (int b = 0; b < XB; ++b) {
+            const int c = c0 + xcol0 + 16 * b + (lane & 15);
+            if (c >= ncols) continue;
+            if constexpr (PAIRED) {
+              part[(size_t)m * part_ld + map.first(c)] = xacc[b][r];
+              part[(size_t)m * part_ld + map.second(c)] = xacc[XB + b][r];
             } else {
-              epi.pair(m, c, v0, v1);
-            }
-          } else {
-            if (part)
               part[(size_t)m * part_ld + c] = xacc[b][r];
-            else
-              epi(m, c, xacc[b][r]);
+            }
+          }
+        }
+      } else if constexpr (PAIRED) {
+        typename Epi::Col xc[XB];
+#pragma unroll
+        for (int b = 0; b < XB; ++b) xc[b] = epi.col(min(c0 + xcol0 + 16 * b + (lane & 15), ncols - 1));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + BM + 4 * (lane >> 4) + r;
+          if (m >= M) continue;
+#pragma unroll
+          for (int b = 0; b < XB; ++b)
+            if (c0 + xcol0 + 16 * b + (lane & 15) < ncols) epi.pair(m, xc[b], xacc[b][r], xacc[XB + b][r]);
+        }
+      } else {
+        // residual epilogues read every old value before the first store
+        // (unconditional, clamped loads, all in flight at once)
+        if constexpr (Epi::kRmw) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + BM + 4 * (lane >> 4) + r;
+#pragma unroll
+            for (int b = 0; b < XB; ++b) {
+              const int c = c0 + xcol0 + 16 * b + (lane & 15);
+              const float old = epi.load(min(m, M - 1), min(c, ncols - 1));
+              xacc[b][r] += (m < M && c < ncols) ? old : 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + BM + 4 * (lane >> 4) + r;
+#pragma unroll
+          for (int b = 0; b < XB; ++b) {
+            const int c = c0 + xcol0 + 16 * b + (lane & 15);
+            if (m < M && c < ncols) epi.store(m, c, xacc[b][r]);
           }
         }
       }
     }
   }
+  auto row_of = [&](int i, int r) { return m0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
+  if (part) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      if (m >= M) continue;
-      if constexpr (PAIRED) {
+      for (int r = 0; r < 16; ++r) {
+        const int m = row_of(i, r);
+        if (m >= M) continue;
+        if constexpr (PAIRED) {
 #pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          const int p = c0 + wn * (WN / 2) + j * 32 + lr;
-          if (p >= ncols) continue;
-          const float v0 = acc[i][j][r], v1 = acc[i][j + TN / 2][r];
-          if (part) {
-            part[(size_t)m * part_ld + map.first(p)] = v0;
-            part[(size_t)m * part_ld + map.second(p)] = v1;
-          } else {
-            epi.pair(m, p, v0, v1);
+          for (int j = 0; j < TN / 2; ++j) {
+            const int p = c0 + wn * (WN / 2) + j * 32 + lr;
+            if (p >= ncols) continue;
+            part[(size_t)m * part_ld + map.first(p)] = acc[i][j][r];
+            part[(size_t)m * part_ld + map.second(p)] = acc[i][j + TN / 2][r];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int n = c0 + wn * WN + j * 32 + lr;
+            if (n < ncols) part[(size_t)m * part_ld + n] = acc[i][j][r];
           }
         }
-      } else {
+      }
+    }
+  } else if constexpr (PAIRED) {
+    typename Epi::Col cols[TN / 2];
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j) cols[j] = epi.col(min(c0 + wn * (WN / 2) + j * 32 + lr, ncols - 1));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = row_of(i, r);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j)
+          if (c0 + wn * (WN / 2) + j * 32 + lr < ncols) epi.pair(m, cols[j], acc[i][j][r], acc[i][j + TN / 2][r]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      // residual epilogues read a 32-row block's old values before its
+      // first store (unconditional, clamped loads: no branch between a load
+      // and its use, so they are all in flight at once)
+      if constexpr (Epi::kRmw) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = row_of(i, r);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int n = c0 + wn * WN + j * 32 + lr;
+            const float old = epi.load(min(m, M - 1), min(n, ncols - 1));
+            acc[i][j][r] += (m < M && n < ncols) ? old : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = row_of(i, r);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int n = c0 + wn * WN + j * 32 + lr;
-          if (n >= ncols) continue;
-          if (part)
-            part[(size_t)m * part_ld + n] = acc[i][j][r];
-          else
-            epi(m, n, acc[i][j][r]);
+          if (m < M && n < ncols) epi.store(m, n, acc[i][j][r]);
         }
       }
     }
