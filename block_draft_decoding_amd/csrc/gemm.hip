@@ -448,6 +448,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
         typename Epi::Col xc[XB];
 #pragma unroll
         for (int b = 0; b < XB; ++b) xc[b] = epi.col(min(c0 + xcol0 + 16 * b + (lane & 15), ncols - 1));
+        wait_vm0();  // column state loaded before the first store
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + BM + 4 * (lane >> 4) + r;
@@ -512,6 +513,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     typename Epi::Col cols[TN / 2];
 #pragma unroll
     for (int j = 0; j < TN / 2; ++j) cols[j] = epi.col(min(c0 + wn * (WN / 2) + j * 32 + lr, ncols - 1));
+    wait_vm0();  // column state loaded before the first store
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll

@@ -39,6 +39,12 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // fall back to full waits before every MFMA group.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their maximum), as the
+// builtin: loads it covers count as complete in the compiler's own tracking,
+// which otherwise re-waits for them, and for every store issued since, at
+// each later use on a path where it could not prove them complete.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
