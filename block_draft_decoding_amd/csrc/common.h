@@ -64,6 +64,7 @@ struct ValueStore<float> {
 };
 template <>
 struct ValueStore<bf16_t> {
+  static __device__ __forceinline__ uint16_t bits(float v) { return bf16_value_as_f16(v); }
   static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = bf16_value_as_f16(v); }
 };
 
@@ -89,12 +90,51 @@ __device__ __forceinline__ bool arg_better(float v1, int c1, float v2, int c2) {
 // division here cost more than the rest of the gate/up epilogue.
 __device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// m = q n + r with 0 <= r < n, for 0 <= m < 2^24, from inv_n = 1 / n rounded
+// to float: the product m * inv_n is within one of m / n, so one correction
+// step makes the quotient exact (checked on the host for n up to 2^24 - 1).
+// About six instructions instead of a general integer division.
+__device__ __forceinline__ void divmod_rows(int m, int n, float inv_n, int& q, int& r) {
+  q = (int)((float)m * inv_n);
+  r = m - q * n;
+  if (r < 0) {
+    --q;
+    r += n;
+  } else if (r >= n) {
+    ++q;
+    r -= n;
+  }
+}
+
 // Rotary embedding constants: the rotation of pair i advances by
 // theta^(-2i/d) / (2 pi) turns per position, computed on the host in double
 // precision (d/2 <= 64 entries).
 struct RopeTab {
   double inv_rev[64];
 };
+
+// cos and sin of pos * inv_rev turns, the turn count reduced to [0, 1) in
+// double precision and evaluated by the hardware sine/cosine (which take
+// turns).
+__device__ __forceinline__ void rope_cs(int pos, double inv_rev, float& c, float& s) {
+  const double r = (double)pos * inv_rev;
+  const float t = (float)(r - floor(r));
+  s = __builtin_amdgcn_sinf(t);
+  c = __builtin_amdgcn_cosf(t);
+}
+// (x0, x1) rotated by the angle with cosine c and sine s.
+__device__ __forceinline__ void rope_rot(float& x0, float& x1, float c, float s) {
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x1 * c + x0 * s;
+  x0 = y0;
+  x1 = y1;
+}
+// Advances (c, s) by one position step (cos and sin of inv_rev turns).
+__device__ __forceinline__ void rope_step(float& c, float& s, float cd, float sd) {
+  const float c2 = c * cd - s * sd;
+  s = s * cd + c * sd;
+  c = c2;
+}
 
 // Rotates the pair (x_i, x_{i + d/2}) by pos * inv_rev turns.  The turn count
 // is reduced to [0, 1) in double precision (exact enough for any position

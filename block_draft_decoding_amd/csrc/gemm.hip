@@ -71,16 +71,73 @@ struct EpiQkv {
   T *q, *k, *vt;
   int L, Lp, nq, nkv, d, half, pos0, rope;
   RopeTab tab;
+  float inv_L;  // 1 / L (rows m < 2^24 split into (b, l) by divmod_rows)
   struct Col {
     int head, i;
     double inv_rev;
+    float cd, sd;  // cos, sin of one position step
   };
   __device__ Col col(int p) const {
     const int i = p % half;
-    return Col{p / half, i, tab.inv_rev[i]};
+    const float st = (float)tab.inv_rev[i];
+    return Col{p / half, i, tab.inv_rev[i], __builtin_amdgcn_cosf(st), __builtin_amdgcn_sinf(st)};
+  }
+  // Four consecutive rows m0 .. m0 + nv - 1 (nv <= 4) of one column pair:
+  // within one request the row offset, the output addresses and the
+  // rotation advance by one step per row (the angle of the first row is
+  // evaluated, the next three follow by rotating it, ~1e-7 apart).
+  __device__ void pair4(int m0, int nv, const Col& c, f32x4_t x0, f32x4_t x1) const {
+    int b, l;
+    divmod_rows(m0, L, inv_L, b, l);
+    if (nv < 4 || l + 3 >= L) {
+      for (int r = 0; r < nv; ++r) pair(m0 + r, c, x0[r], x1[r]);
+      return;
+    }
+    if (c.head < nq + nkv) {
+      if (rope) {
+        float cs, sn;
+        rope_cs(pos0 + l, c.inv_rev, cs, sn);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a0 = x0[r], a1 = x1[r];
+          rope_rot(a0, a1, cs, sn);
+          x0[r] = a0;
+          x1[r] = a1;
+          if (r < 3) rope_step(cs, sn, c.cd, c.sd);
+        }
+      }
+      T* dst = (c.head < nq ? q + (((size_t)b * nq + c.head) * L + l) * d
+                            : k + (((size_t)b * nkv + (c.head - nq)) * L + l) * d) + c.i;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Elem<T>::st(dst + (size_t)r * d, x0[r]);
+        Elem<T>::st(dst + (size_t)r * d + half, x1[r]);
+      }
+    } else {
+      T* dst = vt + (((size_t)b * nkv + (c.head - nq - nkv)) * d + c.i) * Lp + l;
+      T* dst1 = dst + (size_t)half * Lp;
+      if constexpr (sizeof(T) == 2) {
+        if ((l & 3) == 0 && (Lp & 3) == 0) {  // four values of a d-major row: one 8-byte store each
+          u32x2_t w0, w1;
+          w0[0] = ValueStore<T>::bits(x0[0]) | ((uint32_t)ValueStore<T>::bits(x0[1]) << 16);
+          w0[1] = ValueStore<T>::bits(x0[2]) | ((uint32_t)ValueStore<T>::bits(x0[3]) << 16);
+          w1[0] = ValueStore<T>::bits(x1[0]) | ((uint32_t)ValueStore<T>::bits(x1[1]) << 16);
+          w1[1] = ValueStore<T>::bits(x1[2]) | ((uint32_t)ValueStore<T>::bits(x1[3]) << 16);
+          *(u32x2_t*)dst = w0;
+          *(u32x2_t*)dst1 = w1;
+          return;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ValueStore<T>::st(dst + r, x0[r]);
+        ValueStore<T>::st(dst1 + r, x1[r]);
+      }
+    }
   }
   __device__ void pair(int m, const Col& c, float x0, float x1) const {
-    const int b = m / L, l = m - b * L;
+    int b, l;
+    divmod_rows(m, L, inv_L, b, l);
     if (c.head < nq + nkv) {
       if (rope) rope_pair(x0, x1, pos0 + l, c.inv_rev);
       T* dst = c.head < nq ? q + (((size_t)b * nq + c.head) * L + l) * d
@@ -101,16 +158,69 @@ struct EpiCtx {
   T *k, *vt;
   int C, cap, nkv, d, half, pos0, rope;
   RopeTab tab;
+  float inv_C;  // 1 / C
   struct Col {
     int head, i;
     double inv_rev;
+    float cd, sd;  // cos, sin of one position step
   };
   __device__ Col col(int p) const {
     const int i = p % half;
-    return Col{p / half, i, tab.inv_rev[i]};
+    const float st = (float)tab.inv_rev[i];
+    return Col{p / half, i, tab.inv_rev[i], __builtin_amdgcn_cosf(st), __builtin_amdgcn_sinf(st)};
+  }
+  // Four consecutive rows (as EpiQkv::pair4).
+  __device__ void pair4(int m0, int nv, const Col& cc, f32x4_t x0, f32x4_t x1) const {
+    int b, c;
+    divmod_rows(m0, C, inv_C, b, c);
+    if (nv < 4 || c + 3 >= C) {
+      for (int r = 0; r < nv; ++r) pair(m0 + r, cc, x0[r], x1[r]);
+      return;
+    }
+    if (cc.head < nkv) {
+      if (rope) {
+        float cs, sn;
+        rope_cs(pos0 + c, cc.inv_rev, cs, sn);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a0 = x0[r], a1 = x1[r];
+          rope_rot(a0, a1, cs, sn);
+          x0[r] = a0;
+          x1[r] = a1;
+          if (r < 3) rope_step(cs, sn, cc.cd, cc.sd);
+        }
+      }
+      T* dst = k + (((size_t)b * nkv + cc.head) * cap + c) * d + cc.i;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Elem<T>::st(dst + (size_t)r * d, x0[r]);
+        Elem<T>::st(dst + (size_t)r * d + half, x1[r]);
+      }
+    } else {
+      T* dst = vt + (((size_t)b * nkv + (cc.head - nkv)) * d + cc.i) * cap + c;
+      T* dst1 = dst + (size_t)half * cap;
+      if constexpr (sizeof(T) == 2) {
+        if ((c & 3) == 0 && (cap & 3) == 0) {
+          u32x2_t w0, w1;
+          w0[0] = ValueStore<T>::bits(x0[0]) | ((uint32_t)ValueStore<T>::bits(x0[1]) << 16);
+          w0[1] = ValueStore<T>::bits(x0[2]) | ((uint32_t)ValueStore<T>::bits(x0[3]) << 16);
+          w1[0] = ValueStore<T>::bits(x1[0]) | ((uint32_t)ValueStore<T>::bits(x1[1]) << 16);
+          w1[1] = ValueStore<T>::bits(x1[2]) | ((uint32_t)ValueStore<T>::bits(x1[3]) << 16);
+          *(u32x2_t*)dst = w0;
+          *(u32x2_t*)dst1 = w1;
+          return;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ValueStore<T>::st(dst + r, x0[r]);
+        ValueStore<T>::st(dst1 + r, x1[r]);
+      }
+    }
   }
   __device__ void pair(int m, const Col& cc, float x0, float x1) const {
-    const int b = m / C, c = m - b * C;
+    int b, c;
+    divmod_rows(m, C, inv_C, b, c);
     if (cc.head < nkv) {
       if (rope) rope_pair(x0, x1, pos0 + c, cc.inv_rev);
       T* dst = k + (((size_t)b * nkv + cc.head) * cap + c) * d;
@@ -133,6 +243,12 @@ struct EpiGlu {
   __device__ Col col(int p) const { return p; }
   __device__ void pair(int m, int p, float g, float up) const {
     Elem<T>::st(u + (size_t)m * I + p, silu_f(g) * up);
+  }
+  __device__ void pair4(int m0, int nv, int p, f32x4_t g, f32x4_t up) const {
+    T* dst = u + (size_t)m0 * I + p;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r < nv) Elem<T>::st(dst + (size_t)r * I, silu_f(g[r]) * up[r]);
   }
 };
 
@@ -449,13 +565,11 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
 #pragma unroll
         for (int b = 0; b < XB; ++b) xc[b] = epi.col(min(c0 + xcol0 + 16 * b + (lane & 15), ncols - 1));
         wait_vm0();  // column state loaded before the first store
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + BM + 4 * (lane >> 4) + r;
-          if (m >= M) continue;
+        const int mx = m0 + BM + 4 * (lane >> 4);  // this lane's four consecutive extra rows
+        if (mx < M) {
 #pragma unroll
           for (int b = 0; b < XB; ++b)
-            if (c0 + xcol0 + 16 * b + (lane & 15) < ncols) epi.pair(m, xc[b], xacc[b][r], xacc[XB + b][r]);
+            if (c0 + xcol0 + 16 * b + (lane & 15) < ncols) epi.pair4(mx, min(4, M - mx), xc[b], xacc[b], xacc[XB + b]);
         }
       } else {
         // residual epilogues read every old value before the first store
@@ -514,15 +628,21 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < TN / 2; ++j) cols[j] = epi.col(min(c0 + wn * (WN / 2) + j * 32 + lr, ncols - 1));
     wait_vm0();  // column state loaded before the first store
+    // registers 4 q .. 4 q + 3 of a sub-tile hold four consecutive rows
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = row_of(i, r);
+      for (int q = 0; q < 4; ++q) {
+        const int m = row_of(i, 4 * q);
         if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j)
-          if (c0 + wn * (WN / 2) + j * 32 + lr < ncols) epi.pair(m, cols[j], acc[i][j][r], acc[i][j + TN / 2][r]);
+          if (c0 + wn * (WN / 2) + j * 32 + lr < ncols) {
+            const f32x4_t x0 = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            const f32x4_t x1 = {acc[i][j + TN / 2][4 * q], acc[i][j + TN / 2][4 * q + 1], acc[i][j + TN / 2][4 * q + 2],
+                                acc[i][j + TN / 2][4 * q + 3]};
+            epi.pair4(m, min(4, M - m), cols[j], x0, x1);
+          }
       }
     }
   } else {
@@ -640,7 +760,8 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(const float* __restrict
     for (int k = 0; k < 2; ++k) {
       const int m = m0 + rr + 16 * k;
       if (m >= M) continue;
-      const int b = m / e.L, l = m - b * e.L;
+      int b, l;
+      divmod_rows(m, e.L, e.inv_L, b, l);
       if (e.rope) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -673,7 +794,8 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(const float* __restrict
   const int r = tid % RB;
   const int m = m0 + r;
   if (m >= M) return;
-  const int b = m / e.L, l = m - b * e.L;
+  int b, l;
+  divmod_rows(m, e.L, e.inv_L, b, l);
   bf16_t* dst = e.vt + ((size_t)b * e.nkv + (head - e.nq - e.nkv)) * D * e.Lp + l;
   for (int dd = tid / RB; dd < D; dd += 256 / RB) dst[(size_t)dd * e.Lp] = bf16_value_as_f16(vt[dd][r]);
 }
@@ -972,7 +1094,7 @@ hipError_t gemm_qkv(int dt, const void* A, int M, int K, const Wt& Wqkv, const Q
   const int nw = (o.nq + 2 * o.nkv) * o.d;
   if (dt == FPD_DTYPE_BF16) {
     EpiQkv<bf16_t> e{(bf16_t*)o.q, (bf16_t*)o.k, (bf16_t*)o.vt, o.L, o.Lp, o.nq, o.nkv, o.d, half,
-                     o.pos0, o.rope, o.tab};
+                     o.pos0, o.rope, o.tab, 1.0f / (float)o.L};
     GemmPlan pl = plan_gemm_bf16(M, pairs, K, nw, true, /*wide=*/false);
     if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) {
       pl.splits = 1;
@@ -1005,7 +1127,7 @@ hipError_t gemm_qkv(int dt, const void* A, int M, int K, const Wt& Wqkv, const Q
     return hipGetLastError();
   }
   EpiQkv<float> e{(float*)o.q, (float*)o.k, (float*)o.vt, o.L, o.Lp, o.nq, o.nkv, o.d, half,
-                  o.pos0, o.rope, o.tab};
+                  o.pos0, o.rope, o.tab, 1.0f / (float)o.L};
   return run_f32<true>(A, K, M, K, Wqkv, MapRope{half}, pairs, e, st, "gemm_qkv");
 }
 
@@ -1015,11 +1137,13 @@ hipError_t gemm_ctx_kv(int dt, const void* Zn, int M, int K, const Wt& Wkv, cons
   const int pairs = 2 * o.nkv * half;
   const int nw = 2 * o.nkv * o.d;
   if (dt == FPD_DTYPE_BF16) {
-    EpiCtx<bf16_t> e{(bf16_t*)o.k, (bf16_t*)o.vt, o.C, o.cap, o.nkv, o.d, half, o.pos0, o.rope, o.tab};
+    EpiCtx<bf16_t> e{(bf16_t*)o.k, (bf16_t*)o.vt, o.C, o.cap, o.nkv, o.d, half, o.pos0, o.rope, o.tab,
+                     1.0f / (float)o.C};
     return run_bf16<true>(Zn, K, M, K, Wkv, MapRope{half}, pairs, nw, e, partial, partial_bytes, st,
                           "gemm_ctx_kv");
   }
-  EpiCtx<float> e{(float*)o.k, (float*)o.vt, o.C, o.cap, o.nkv, o.d, half, o.pos0, o.rope, o.tab};
+  EpiCtx<float> e{(float*)o.k, (float*)o.vt, o.C, o.cap, o.nkv, o.d, half, o.pos0, o.rope, o.tab,
+                  1.0f / (float)o.C};
   return run_f32<true>(Zn, K, M, K, Wkv, MapRope{half}, pairs, e, st, "gemm_ctx_kv");
 }
 
