@@ -112,12 +112,14 @@ def test_small_bf16_end_to_end(kind, B, C, over):
 # 4L packed rows per KV head (n_q = 8, n_kv = 2): L = 65 and 72 end in a
 # tail tile of 4 and 32 rows, which runs in its own two-split workgroups
 # while the full tile takes 3 (C = 300) or 7 (C = 1000) key splits; L = 73
-# leaves 36 rows, more than one wave holds, and keeps the plain plan.
-@pytest.mark.parametrize("B,C,L", [(2, 300, 65), (1, 1000, 72), (2, 300, 73)])
-def test_tail_query_tile(B, C, L):
-    wl = small_workload("text", B, C, seed=80 + L, block_len=L)
+# leaves 36 rows, more than one wave holds, and keeps the plain plan.  The
+# shared case has three blocks read one context through the tail workgroups.
+@pytest.mark.parametrize("B,C,L,shared", [(2, 300, 65, False), (1, 1000, 72, False), (2, 300, 73, False),
+                                          (3, 300, 65, True)])
+def test_tail_query_tile(B, C, L, shared):
+    wl = small_workload("text", B, C, seed=80 + L, block_len=L, shared_ctx=shared)
     inp, g, lg, res = run_both(wl)
-    compare_all(wl, g, lg, res, "bf16", f"tail tile B={B} C={C} L={L}", inp.weights.w_lm)
+    compare_all(wl, g, lg, res, "bf16", f"tail tile B={B} C={C} L={L} shared={shared}", inp.weights.w_lm)
 
 
 def test_head_without_k_groups():
