@@ -11,6 +11,13 @@ in HBM.  Context fusion (fpd_fuse_context_kv) runs once per context and is
 timed and reported separately.  The default workload is the 64-waypoint
 2D+3D trajectory primitive (L = 385, context 4,096, bf16, batch 1).
 
+With --graph the step is also captured into a HIP graph (the library only
+enqueues kernels on the caller's stream, so its launches capture as they
+are), its outputs are checked bitwise against an eager step, and the
+timed steps replay it; the eager time per step is reported beside it.
+Replay measured about 1% slower than eager launches at L = 385 and 25, so
+eager launches are the default.
+
 Prints one JSON line.  The dominant kernel's roofline uses HIP events
 recorded by the library around its launches (same stream) over a second
 pass of the timed steps; the CPU baseline is the float64 oracle on the
@@ -157,6 +164,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="traj2d3d")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="time replays of the step captured into a HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bounded sample)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 256 MiB device buffer 5 times (reference for the FETCH_SIZE / WRITE_SIZE "
@@ -229,20 +237,39 @@ def main():
         else:
             fpd.fpd_validate_primitive(lay, toks, k_out, aux, stream=stream)
 
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
+    def timed(run_step):
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                run_step()
+            stream.synchronize()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            ev[0].record(stream)
+            for i in range(args.steps):
+                run_step()
+                ev[i + 1].record(stream)
+            stream.synchronize()
+            torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)], ev[0].elapsed_time(ev[-1]) / args.steps
+
+    per_eager, eager_ms = timed(step)
+    launch = "eager"
+    per, ms = per_eager, eager_ms
+    if args.graph:
+        ref = [x.clone() for x in (hidden, toks, k_out, aux)]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
             step()
+        for x in (hidden, toks, k_out, aux):
+            x.zero_()
+        with torch.cuda.stream(stream):
+            graph.replay()
         stream.synchronize()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        ev[0].record(stream)
-        for i in range(args.steps):
-            step()
-            ev[i + 1].record(stream)
-        stream.synchronize()
-        torch.cuda.synchronize()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+        for a, b in zip((hidden, toks, k_out, aux), ref):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay differs from the eager step")
+        per, ms = timed(graph.replay)
+        launch = "hip_graph"
     drafted = B * (L - 1)
 
     # context fusion, once per context (reported, not in the step)
@@ -359,6 +386,8 @@ def main():
         "fuse_context_ms": round(fuse_ms, 4),
         f"append_context_{n_app}_ms": round(append_ms, 4),
         "decode_coords_ms": round(decode_ms, 4),
+        "launch": launch,
+        "eager_ms_per_step": round(eager_ms, 4),
         "cold_ms_per_step": round(fuse_ms + ms, 4),
         "accepted_k": k_out[:8].tolist(),
         "roofline": roof,
