@@ -385,6 +385,11 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     const int m = min(m0 + r, M - 1);
     xoff[i] = (uint32_t)(((size_t)m * lda + c * 8) * 2 + (lane & 3) * 4);
   }
+  // With one row tile every weight tile is read by one workgroup only: the
+  // small-row tiles then load it non-temporal (trajectory L = 25 block
+  // 0.450 -> 0.437 ms).  Where row tiles share weight tiles through L2 the
+  // same hint cost 5% (L = 385), so larger tiles keep the default policy.
+  const bool w_once = BM <= 64 && m_tiles == 1;
   auto issue = [&](int kt, int stage, auto ext_c) {
     const int soff = kt * BK * 2;
     const int k0 = kt * BK, sb = w_tiled ? (k0 / 64) * 4096 + (k0 % 64) * 2 : soff;
@@ -392,8 +397,14 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     u32x4_t* base = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < AI; ++i) lds_dma16(arsrc, base + (wave * AI + i) * 64, aoff[i], soff);
+    if (w_once) {
 #pragma unroll
-    for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + AR * CH + (wave * BI + i) * 64, boff[i], sb);
+      for (int i = 0; i < BI; ++i)
+        lds_dma16<kLoadNonTemporal>(brsrc, base + AR * CH + (wave * BI + i) * 64, boff[i], sb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + AR * CH + (wave * BI + i) * 64, boff[i], sb);
+    }
     if constexpr (decltype(ext_c)::value) {
 #pragma unroll
       for (int i = 0; i < XI; ++i) lds_dma4(arsrc, base + BM * CH + (wave * XI + i) * 16, xoff[i], soff);

@@ -6,12 +6,18 @@
 
 namespace fpd {
 
+// Cache-policy operand of a buffer load: non-temporal (the nt bit).
+constexpr int kLoadNonTemporal = 2;
+
 // One 16-byte buffer load per lane written straight into LDS: lane i fills
-// the 16 bytes at dst + 16 i (dst is wave-uniform).  Only the device pass
-// sees the builtin; the host pass would otherwise drop the kernel stubs.
+// the 16 bytes at dst + 16 i (dst is wave-uniform).  POLICY is the load's
+// cache-policy operand.  Only the device pass sees the builtin; the host
+// pass would otherwise drop the kernel stubs.
+template <int POLICY = 0>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, u32x4_t* dst, uint32_t voff, int soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0,
+                                           POLICY);
 #endif
 }
 
