@@ -74,6 +74,13 @@ struct AttnP {
   float scale_log2;
 };
 
+// max(x, x of lane l ^ 32) without an LDS round trip: v_permlane32_swap with
+// x as both operands returns (x[l mod 32], x[l mod 32 + 32]) in every lane l.
+__device__ __forceinline__ float max_lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // LDS tiles hold 16-byte chunks without padding; chunk positions are XOR
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(AW * 64) void attn_bf16_kernel(AttnP p) {
               mloc = fmaxf(mloc, s[i][r]);
             }
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        mloc = max_lane_xor32(mloc);
         // keep the reference max unless it would let exponents exceed 2^kRescale
         const bool grow = (mloc - m_run) * p.scale_log2 > kRescale;
         if (__builtin_amdgcn_ballot_w64(grow)) {
