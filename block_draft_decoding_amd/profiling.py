@@ -84,7 +84,8 @@ def stats_markdown(stats_csv: str, title: str, command: str, bench_json: Optiona
         with open(bench_json) as f:
             b = json.loads(f.read().strip().splitlines()[-1])
         r = b["roofline"]
-        lines += ["", f"bench.py line of the same build: {b['value']:.0f} drafted tokens/s, {b['ms_per_step']} ms "
+        lines += ["", f"bench.py line of the same build (same command without the profiler, run right after "
+                      f"it): {b['value']:.0f} drafted tokens/s, {b['ms_per_step']} ms "
                       f"per block; dominant kernel `{r['kernel']}` {r['avg_launch_ms'] * 1e3:.1f} µs per launch "
                       f"({r['achieved']} {r['unit']}, {100 * r['frac']:.1f}% of peak)."]
     lines += ["", f"Library source digest: `{source_digest()}`"]
