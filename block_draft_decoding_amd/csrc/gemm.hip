@@ -259,12 +259,28 @@ struct EpiGlu {
 // go first and the last, partly filled row tile of each column (cheap: its
 // empty row blocks are skipped) goes last, where it fills the gaps the full
 // tiles leave.  m_full = number of full row tiles (m_tiles or m_tiles - 1).
-__device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, int m_full) {
+//
+// With many row tiles (kGroupMinRows or more, all full) the range instead
+// walks groups of kGroupRows row tiles across every column tile, so that the
+// ~32 tiles an XCD runs at once are 4 row tiles x 8 column tiles: each A
+// K-slab is then read by 8 tiles and each weight K-slab by 4 out of that L2,
+// where row tiles first would have 32 tiles stream 32 different A slabs past
+// one weight slab, re-reading all of A once per column tile.
+constexpr int kGroupRows = 4;
+constexpr int kGroupMinRows = 16;
+__device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, int m_full, int n_tiles) {
   const int x = bid % kXcds, local = bid / kXcds;
   const int per = grid / kXcds, rem = grid % kXcds;
   const int s = x * per + (x < rem ? x : rem);
   const int cnt = per + (x < rem ? 1 : 0);
-  if (m_full == m_tiles) return s + local;
+  if (m_full == m_tiles) {
+    const int t = s + local;
+    if (m_tiles < kGroupMinRows) return t;
+    const int mn = m_tiles * n_tiles, ks = t / mn, r = t % mn;
+    const int g = r / (kGroupRows * n_tiles), w = r % (kGroupRows * n_tiles);
+    const int gm = min(kGroupRows, m_tiles - g * kGroupRows);  // row tiles of this group
+    return ks * mn + (w / gm) * m_tiles + g * kGroupRows + w % gm;
+  }
   auto full_before = [&](int t) { return (t / m_tiles) * m_full + min(t % m_tiles, m_full); };
   const int h0 = full_before(s), h1 = full_before(s + cnt);
   if (local < h1 - h0) {
@@ -330,7 +346,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const bool loader = wave < LW;
-  const int tile = gemm_tile_order(blockIdx.x, gridDim.x, m_tiles, M / BM);
+  const int tile = gemm_tile_order(blockIdx.x, gridDim.x, m_tiles, M / BM, n_tiles);
   const int mt = tile % m_tiles;
   const int rest = tile / m_tiles;
   const int nt = rest % n_tiles;
