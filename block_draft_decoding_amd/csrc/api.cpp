@@ -77,9 +77,9 @@ struct DraftWs {
   size_t partial_bytes, attn_bytes;
 };
 
-size_t gemm_partial_bytes(int dt, int M, int ncols, int K, int nw, bool paired, bool wide = true) {
+size_t gemm_partial_bytes(int dt, int M, int ncols, int K, int nw, bool paired) {
   if (dt != FPD_DTYPE_BF16) return 0;
-  return plan_gemm_bf16(M, ncols, K, nw, paired, wide).partial_floats * sizeof(float);
+  return plan_gemm_bf16(M, ncols, K, nw, paired).partial_floats * sizeof(float);
 }
 
 DraftWs plan_draft(const fpd_drafter& d, int B, int L, int C) {
@@ -103,7 +103,7 @@ DraftWs plan_draft(const fpd_drafter& d, int B, int L, int C) {
   const int dt = c.dtype, m = (int)M, qd = c.n_q * c.head_dim;
   size_t pb = 0;
   pb = std::max(pb, gemm_partial_bytes(dt, m, (c.n_q + 2 * c.n_kv) * c.head_dim / 2, c.hidden,
-                                       (c.n_q + 2 * c.n_kv) * c.head_dim, true, /*wide=*/false));
+                                       (c.n_q + 2 * c.n_kv) * c.head_dim, true));
   // O and the MLP run on all rows, and in the last layer of a single block on L - 1
   for (const int mr : {m, B == 1 ? L - 1 : m}) {
     pb = std::max(pb, gemm_partial_bytes(dt, mr, c.hidden, qd, c.hidden, false));

@@ -48,9 +48,7 @@ int gemm_cfg_bk(int cfg);
 int gemm_cfg_extra_rows(int cfg, bool paired);
 // M rows, ncols logical output columns (pairs for paired epilogues), K depth,
 // nw = W rows covered (partial row length), paired = two W rows per column.
-// wide: 256x256 tiles may be chosen when they give two or more passes of
-// workgroups (off for the scattered q/k/v epilogue, which measured no gain).
-GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired, bool wide = true);
+GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired);
 
 // ---- K-tile-contiguous copies of the weights ----------------------------------
 // A projection's weights: row-major W [rows, K] (torch Linear layout) and,

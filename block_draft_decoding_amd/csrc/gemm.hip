@@ -1019,14 +1019,15 @@ GemmPlan make_plan(int cfg, int M, int ncols, int K, int nw, bool paired, int sp
 // that the row tiles (a partly filled last one counts its share of 32-row
 // blocks) cover about 80% of the CUs once; narrow plain outputs take 64x128 tiles
 // split along K.
-GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired, bool wide) {
+GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   const int kt = K / 64;
   // Many rows (the 8-request point-motion block, M = 19,464): 256x256 tiles
   // move half the operand bytes per MFMA of 128x256 ones, which is what the
   // per-CU operand fill rate bounds; with the last tile carrying up to 16
   // leftover rows they took gate/up 1.93 -> 1.64 ms, down 1.21 -> 1.02 ms and
-  // O 0.61 -> 0.55 ms per launch there (q/k/v: no gain).
-  if (wide) {
+  // O 0.61 -> 0.55 ms per launch there, and q/k/v 0.70 -> 0.63 ms once the
+  // tile order grouped row tiles.
+  {
     const GemmPlan w256 = make_plan(GEMM_256x256_W8_S2, M, ncols, K, nw, paired, 1, /*fold=*/true);
     if (w256.m_tiles * w256.n_tiles >= 512) return w256;
   }
@@ -1122,7 +1123,7 @@ hipError_t gemm_qkv(int dt, const void* A, int M, int K, const Wt& Wqkv, const Q
   if (dt == FPD_DTYPE_BF16) {
     EpiQkv<bf16_t> e{(bf16_t*)o.q, (bf16_t*)o.k, (bf16_t*)o.vt, o.L, o.Lp, o.nq, o.nkv, o.d, half,
                      o.pos0, o.rope, o.tab, 1.0f / (float)o.L};
-    GemmPlan pl = plan_gemm_bf16(M, pairs, K, nw, true, /*wide=*/false);
+    GemmPlan pl = plan_gemm_bf16(M, pairs, K, nw, true);
     if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) {
       pl.splits = 1;
       pl.partial_floats = 0;
