@@ -403,7 +403,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   }
   // With one row tile every weight tile is read by one workgroup only: the
   // small-row tiles then load it non-temporal (trajectory L = 25 block
-  // 0.450 -> 0.437 ms).  Where row tiles share weight tiles through L2 the
+  // 0.450 -> 0.440 ms).  Where row tiles share weight tiles through L2 the
   // same hint cost 5% (L = 385), so larger tiles keep the default policy.
   const bool w_once = BM <= 64 && m_tiles == 1;
   auto issue = [&](int kt, int stage, auto ext_c) {
@@ -1027,10 +1027,8 @@ GemmPlan plan_gemm_bf16(int M, int ncols, int K, int nw, bool paired) {
   // leftover rows they took gate/up 1.93 -> 1.64 ms, down 1.21 -> 1.02 ms and
   // O 0.61 -> 0.55 ms per launch there, and q/k/v 0.70 -> 0.63 ms once the
   // tile order grouped row tiles.
-  {
-    const GemmPlan w256 = make_plan(GEMM_256x256_W8_S2, M, ncols, K, nw, paired, 1, /*fold=*/true);
-    if (w256.m_tiles * w256.n_tiles >= 512) return w256;
-  }
+  const GemmPlan w256 = make_plan(GEMM_256x256_W8_S2, M, ncols, K, nw, paired, 1, /*fold=*/true);
+  if (w256.m_tiles * w256.n_tiles >= 512) return w256;
   auto with_splits = [&](int cfg, int lo, int hi) {
     GemmPlan p = make_plan(cfg, M, ncols, K, nw, paired, 1);
     const int tiles = p.m_tiles * p.n_tiles;
