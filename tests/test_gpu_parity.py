@@ -109,6 +109,15 @@ def test_small_bf16_end_to_end(kind, B, C, over):
         progress(f"[pairs] off-frame tokens {n_off} of {res['tokens'].size}")
 
 
+# Context fusion over B x C = 4,096 rows takes 32 row tiles of 128 (split K
+# two ways), so the GEMM launch walks its tiles in groups of four row tiles
+# across the column tiles; ctx_k / ctx_v are compared row by row.
+def test_grouped_tile_order_context_fusion():
+    wl = small_workload("traj2d3d", 2, 2048, seed=47, n_points=7, off_id=4099 - 1020 + 1002)
+    inp, g, lg, res = run_both(wl)
+    compare_all(wl, g, lg, res, "bf16", "grouped tile order B=2 C=2048", inp.weights.w_lm)
+
+
 # 4L packed rows per KV head (n_q = 8, n_kv = 2): L = 65 and 72 end in a
 # tail tile of 4 and 32 rows, which runs in its own two-split workgroups
 # while the full tile takes 3 (C = 300) or 7 (C = 1000) key splits; L = 73
