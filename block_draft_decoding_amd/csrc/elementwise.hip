@@ -77,6 +77,28 @@ __device__ __forceinline__ void store_norm4<float>(float* dst, f32x4_t v, float 
   *(f32x4_t*)dst = v * inv * gg;
 }
 
+// The same with the 4 weights loaded beforehand (so that their load can go
+// out with the row's other loads).
+template <class T>
+struct Gamma4;
+template <>
+struct Gamma4<bf16_t> {
+  u32x2_t w;
+  __device__ void load(const bf16_t* g) { w = *(const u32x2_t*)g; }
+  __device__ void store(bf16_t* dst, f32x4_t v, float inv) const {
+    u32x2_t o;
+    o[0] = pack_bf16x2(v[0] * inv * __uint_as_float(w[0] << 16), v[1] * inv * __uint_as_float(w[0] & 0xffff0000u));
+    o[1] = pack_bf16x2(v[2] * inv * __uint_as_float(w[1] << 16), v[3] * inv * __uint_as_float(w[1] & 0xffff0000u));
+    *(u32x2_t*)dst = o;
+  }
+};
+template <>
+struct Gamma4<float> {
+  f32x4_t w;
+  __device__ void load(const float* g) { w = *(const f32x4_t*)g; }
+  __device__ void store(float* dst, f32x4_t v, float inv) const { *(f32x4_t*)dst = v * inv * w; }
+};
+
 // Fused residual update and RMSNorm, one workgroup per row: h[r] +=
 // sum_s partial[s][r] (split-K partial products, fixed split order; none when
 // partial is null), then out[row'] = RMSNorm(h[r]) * g.  With final_L > 0 only
@@ -101,20 +123,35 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
   const int n4 = H / 4;
   const size_t pstride = (size_t)M * H / 4;
   const f32x4_t* pr = partial ? (const f32x4_t*)partial + (size_t)r * n4 : nullptr;
-  f32x4_t v[4];
+  // Every load of the row (residual, partials, norm weights) goes out before
+  // the first use, and one tracked wait covers them all: one memory round
+  // trip, where loading and storing each float4 group in turn cost one per
+  // group (and the compiler's own waits then also waited for the stores).
+  f32x4_t v[4], parts[4][NS];
+  Gamma4<T> gw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * 256;
+    if (k < n4) {
+      v[i] = hr[k];
+      gw[i].load(g + 4 * k);
+      if (pr) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) parts[i][s] = pr[s * pstride + k];
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), as the builtin so the compiler's own tracking sees it
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k = threadIdx.x + i * 256;
     if (k < n4) {
-      f32x4_t x = hr[k];
+      f32x4_t x = v[i];
       if (pr) {
-        f32x4_t parts[NS];
+        f32x4_t acc = parts[i][0];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) parts[s] = pr[s * pstride + k];
-        f32x4_t acc = parts[0];
-#pragma unroll
-        for (int s = 1; s < NS; ++s) acc += parts[s];
+        for (int s = 1; s < NS; ++s) acc += parts[i][s];
         x += acc;
         hr[k] = x;
       }
@@ -127,7 +164,7 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k = threadIdx.x + i * 256;
-    if (k < n4) store_norm4<T>(dst + 4 * k, v[i], inv, g + 4 * k);
+    if (k < n4) gw[i].store(dst + 4 * k, v[i], inv);
   }
 }
 
@@ -211,8 +248,9 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* __restri
   const bool ok = t >= 0 && t < V;
   f32x4_t* hr = (f32x4_t*)(h + (size_t)r * H);
   const int n4 = H / 4;
+  // all of the row's loads first, one tracked wait (as in resid_norm_kernel)
   f32x4_t v[4];
-  float ss = 0.f;
+  Gamma4<T> gw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k = threadIdx.x + i * 256;
@@ -223,16 +261,25 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* __restri
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = Elem<T>::ld(src + e);
       }
-      hr[k] = x;
       v[i] = x;
-      ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      gw[i].load(g + 4 * k);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), as the builtin so the compiler's own tracking sees it
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * 256;
+    if (k < n4) {
+      hr[k] = v[i];
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
     }
   }
   const float inv = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k = threadIdx.x + i * 256;
-    if (k < n4) store_norm4<T>(a + (size_t)r * H + 4 * k, v[i], inv, g + 4 * k);
+    if (k < n4) gw[i].store(a + (size_t)r * H + 4 * k, v[i], inv);
   }
 }
 
