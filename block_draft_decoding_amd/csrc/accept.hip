@@ -36,6 +36,24 @@ __device__ __forceinline__ int wave_min(int v) {
 // answer is a workgroup minimum over the first failing positions.
 constexpr int kValThreads = 512;
 
+// Copies n ints to LDS, eight loads in flight per thread (a legal-id table of
+// ~5,000 ids would otherwise take one memory round trip per 512 ids).
+__device__ __forceinline__ void stage_to_lds(const int32_t* __restrict__ src, int n, int32_t* dst) {
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * kValThreads) {
+    int32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kValThreads;
+      v[u] = src[min(i, n - 1)];  // clamped, so every load is unconditional
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kValThreads;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kValThreads) void validate_kernel(ValidateArgs a, int stage_tok, int stage_ids) {
   extern __shared__ int32_t sm[];
   __shared__ int red[2][kValThreads / 64];
@@ -45,30 +63,31 @@ __global__ __launch_bounds__(kValThreads) void validate_kernel(ValidateArgs a, i
   const int32_t* tok = gtok;
   const int32_t* ids = a.set_ids;
   if (stage_tok) {
-    for (int i = tid; i < P; i += kValThreads) sm[i] = gtok[i];
+    stage_to_lds(gtok, P, sm);
     tok = sm;
   }
   if (stage_ids) {
     int32_t* sid = sm + (stage_tok ? P : 0);
-    for (int i = tid; i < a.n_set_ids; i += kValThreads) sid[i] = a.set_ids[i];
+    stage_to_lds(a.set_ids, a.n_set_ids, sid);
     ids = sid;
   }
   __syncthreads();
   int first = INT_MAX, unc = INT_MAX;
   for (int p = tid + 1; p < a.L; p += kValThreads) {
+    // the position's layout entries in one batch of loads (each loaded where
+    // it is used, they made a chain of dependent memory round trips)
+    const int s = a.pos_set[p], q = a.partner[p], w = a.field_w[p];
+    const bool uncertain = a.conf && a.coord[p] && !(a.conf[(size_t)b * P + p - 1] >= a.tau);
     const int t = tok[p - 1];
     // a coordinate is certain only if its confidence reaches tau (NaN fails)
-    if (a.conf && a.coord[p] && !(a.conf[(size_t)b * P + p - 1] >= a.tau)) unc = min(unc, p - 1);
-    const int s = a.pos_set[p];
+    if (uncertain) unc = min(unc, p - 1);
     bool ok;
     if (s == -1)
       ok = t >= 0 && t < a.vocab;
     else
       ok = in_set(ids + a.set_offsets[s], a.set_offsets[s + 1] - a.set_offsets[s], t);
     if (!ok) first = min(first, p - 1);
-    const int q = a.partner[p];
     if (q >= 0 && ((t == a.off_id) != (tok[q - 1] == a.off_id))) first = min(first, p - 1);
-    const int w = a.field_w[p];
     if (w > 0) {  // FILL^j DIGIT^(w-j), j <= w-1
       bool digits = false;
       for (int i = 0; i < w; ++i) {
