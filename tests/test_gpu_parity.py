@@ -111,11 +111,14 @@ def test_small_bf16_end_to_end(kind, B, C, over):
 
 # Context fusion over B x C = 4,096 rows takes 32 row tiles of 128 (split K
 # two ways), so the GEMM launch walks its tiles in groups of four row tiles
-# across the column tiles; ctx_k / ctx_v are compared row by row.
-def test_grouped_tile_order_context_fusion():
-    wl = small_workload("traj2d3d", 2, 2048, seed=47, n_points=7, off_id=4099 - 1020 + 1002)
+# across the column tiles; 2,100 rows end in a partly filled 17th row tile,
+# which keeps the row-tiles-first order with that tile last.  ctx_k / ctx_v
+# are compared row by row.
+@pytest.mark.parametrize("B,C", [(2, 2048), (1, 2100)])
+def test_grouped_tile_order_context_fusion(B, C):
+    wl = small_workload("traj2d3d", B, C, seed=47 + B, n_points=7, off_id=4099 - 1020 + 1002)
     inp, g, lg, res = run_both(wl)
-    compare_all(wl, g, lg, res, "bf16", "grouped tile order B=2 C=2048", inp.weights.w_lm)
+    compare_all(wl, g, lg, res, "bf16", f"grouped tile order B={B} C={C}", inp.weights.w_lm)
 
 
 # 4L packed rows per KV head (n_q = 8, n_kv = 2): L = 65 and 72 end in a
