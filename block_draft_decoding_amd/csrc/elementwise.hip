@@ -25,33 +25,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   for (int k = threadIdx.x; k < H; k += blockDim.x) dst[k] = Elem<T>::ld(src + k);
 }
 
-// One wavefront per output row (4 rows per workgroup), float4 loads:
-// y = x / sqrt(mean(x^2) + eps) * g.  H is a multiple of 64.
-template <class T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, int rows, int per,
-                                                      int in_stride, int in_off, const T* __restrict__ g,
-                                                      float eps, T* __restrict__ y) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const f32x4_t* src = (const f32x4_t*)(x + ((size_t)(r / per) * in_stride + in_off + r % per) * H);
-  const int n4 = H / 4;
-  float ss = 0.f;
-  for (int k = lane; k < n4; k += 64) {
-    const f32x4_t v = src[k];
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  T* dst = y + (size_t)r * H;
-  for (int k = lane; k < n4; k += 64) {
-    const f32x4_t v = src[k];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Elem<T>::st(dst + 4 * k + e, v[e] * inv * Elem<T>::ld(g + 4 * k + e));
-  }
-}
-
+// Sum of a value over the 256 threads of a workgroup (every thread gets it).
 __device__ __forceinline__ float block_sum256(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -98,6 +72,48 @@ struct Gamma4<float> {
   __device__ void load(const float* g) { w = *(const f32x4_t*)g; }
   __device__ void store(float* dst, f32x4_t v, float inv) const { *(f32x4_t*)dst = v * inv * w; }
 };
+
+// One wavefront per output row (4 rows per workgroup), float4 loads:
+// y = x / sqrt(mean(x^2) + eps) * g.  H is a multiple of 64.
+template <class T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, int rows, int per,
+                                                      int in_stride, int in_off, const T* __restrict__ g,
+                                                      float eps, T* __restrict__ y) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const f32x4_t* src = (const f32x4_t*)(x + ((size_t)(r / per) * in_stride + in_off + r % per) * H);
+  const int n4 = H / 4;
+  // the row (H <= 4096: at most 16 float4 per lane) and its norm weights are
+  // loaded once, all before the first use, and kept in registers for the
+  // normalised store (a loop of load-and-wait steps over the row, read twice,
+  // cost 20 memory round trips per row at H = 2560)
+  constexpr int MAXI = 16;
+  f32x4_t v[MAXI];
+  Gamma4<T> gw[MAXI];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int k = lane + i * 64;
+    if (k < n4) {
+      v[i] = src[k];
+      gw[i].load(g + 4 * k);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), as the builtin so the compiler's own tracking sees it
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i)
+    if (lane + i * 64 < n4) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  T* dst = y + (size_t)r * H;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int k = lane + i * 64;
+    if (k < n4) gw[i].store(dst + 4 * k, v[i], inv);
+  }
+}
 
 // Fused residual update and RMSNorm, one workgroup per row: h[r] +=
 // sum_s partial[s][r] (split-K partial products, fixed split order; none when
