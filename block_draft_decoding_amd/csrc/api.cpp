@@ -429,15 +429,22 @@ int32_t fuse_rows(const fpd_drafter* d, const void* feats, int32_t B, int32_t C,
   const fpd_config& c = d->cfg;
   const int dt = c.dtype, H = c.hidden, M = B * C, dh = c.head_dim;
   hipStream_t s = (hipStream_t)stream;
-  const void* X = feats;
-  if (c.n_fused > 1) {
-    FPD_TRY_HIP(concat_features(dt, feats, B, c.n_fused, C, H, wsp(ws, w.x), s));
-    X = wsp(ws, w.x);
-  }
   float* Z = (float*)wsp(ws, w.z);
   float* part = (float*)wsp(ws, w.partial);
-  FPD_TRY_HIP(gemm_store_f32(dt, X, c.n_fused * H, M, c.n_fused * H, Wt{d->w.w_fc, d->t_fc}, H, Z, H, part,
-                             w.partial_bytes, s, "gemm_fc"));
+  if (dt == FPD_DTYPE_BF16) {
+    // the bf16 projection reads the features [B, n_t, C, H] in place as
+    // their concatenation [B * C, n_t * H]
+    FPD_TRY_HIP(gemm_store_fused_f32(feats, B, c.n_fused, C, H, Wt{d->w.w_fc, d->t_fc}, H, Z, H, part,
+                                     w.partial_bytes, s, "gemm_fc"));
+  } else {
+    const void* X = feats;
+    if (c.n_fused > 1) {
+      FPD_TRY_HIP(concat_features(dt, feats, B, c.n_fused, C, H, wsp(ws, w.x), s));
+      X = wsp(ws, w.x);
+    }
+    FPD_TRY_HIP(gemm_store_f32(dt, X, c.n_fused * H, M, c.n_fused * H, Wt{d->w.w_fc, d->t_fc}, H, Z, H, part,
+                               w.partial_bytes, s, "gemm_fc"));
+  }
   void* Zn = wsp(ws, w.zn);
   FPD_TRY_HIP(rmsnorm_rows(dt, Z, H, M, M, 0, 0, d->w.g_fc, c.rms_eps, Zn, s));
   const size_t per_layer = (size_t)B * c.n_kv * ctx_cap * dh * d->esz;

@@ -75,6 +75,11 @@ hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const Wt
                           float* out, int ldo, float* partial, size_t partial_bytes, hipStream_t st,
                           const char* tag);
 
+// The same (bf16 only) with A the per-layer target features [B, n_t, C, H]
+// read in place as their concatenation [B * C, n_t * H] (H a multiple of 64).
+hipError_t gemm_store_fused_f32(const void* feats, int B, int n_t, int C, int H, const Wt& W, int N, float* out,
+                                int ldo, float* partial, size_t partial_bytes, hipStream_t st, const char* tag);
+
 // h[m, n] += Y (float residual).
 hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const Wt& W, int N,
                          float* h, int ldh, float* partial, size_t partial_bytes, hipStream_t st,

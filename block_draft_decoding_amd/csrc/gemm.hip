@@ -308,11 +308,34 @@ __device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, i
 // by 4-byte LDS-writing loads, multiplied by 16x16x32 MFMAs whose columns are
 // split over all waves).  A separate row tile for them would stream the whole
 // weight column once more from HBM for r rows of work.
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int XR, bool PAIRED, class Map, class Epi>
+// Addressing of the A operand (byte offsets for the buffer loads: a per-row
+// part fixed per lane, and a per-K-tile part that is scalar).  APlain: row-
+// major A [M, K], row m at m * lda.  AFused: the per-layer target features
+// [B, n_t, C, H] read in place as their concatenation [B * C, n_t * H] (row
+// b * C + c, column t * H + k; lda = n_t * H), which the context fusion's
+// projection would otherwise copy out first (a 64-deep K tile never crosses
+// a layer, since H is a multiple of 64).
+struct APlain {
+  __device__ uint32_t row(int m, int lda) const { return (uint32_t)((size_t)m * lda * 2); }
+  __device__ int ktile(int kt, int bk) const { return kt * bk * 2; }
+};
+struct AFused {
+  int C, H;  // positions per request, columns of one target layer
+  __device__ uint32_t row(int m, int lda) const {
+    return (uint32_t)(((size_t)(m / C) * C * lda + (size_t)(m % C) * H) * 2);
+  }
+  __device__ int ktile(int kt, int bk) const {
+    const int k = kt * bk;
+    return (int)(((size_t)(k / H) * C * H + k % H) * 2);
+  }
+};
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int XR, bool PAIRED, class Map, class Epi,
+          class ALay = APlain>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, int M, int K, const bf16_t* __restrict__ W, int w_rows, int w_tiled,
     Map map, int ncols, Epi epi, float* __restrict__ partial, int part_ld, int m_tiles, int n_tiles,
-    int splits) {
+    int splits, ALay alay = {}) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int NT = 64 * NW;
   // Waves that fill the ring.  In 8-wave workgroups only waves 0-3 (one per
@@ -375,7 +398,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   for (int i = 0; i < AI; ++i) {
     const int sl = (wave * AI + i) * 64 + lane, r = sl / CH, c = (sl % CH) ^ ((r / (16 / CH)) & (CH - 1));
     const int m = min(m0 + r, M - 1);
-    aoff[i] = (uint32_t)(((size_t)m * lda + c * 8) * 2);
+    aoff[i] = alay.row(m, lda) + (uint32_t)(c * 16);
   }
   uint32_t boff[BI];
 #pragma unroll
@@ -399,7 +422,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     const int q = (wave * XI + i) * 16 + lane / 4, r = BM + q / CH;
     const int c = (q % CH) ^ ((r / (16 / CH)) & (CH - 1));
     const int m = min(m0 + r, M - 1);
-    xoff[i] = (uint32_t)(((size_t)m * lda + c * 8) * 2 + (lane & 3) * 4);
+    xoff[i] = alay.row(m, lda) + (uint32_t)(c * 16 + (lane & 3) * 4);
   }
   // With one row tile every weight tile is read by one workgroup only: the
   // small-row tiles then load it non-temporal (trajectory L = 25 block
@@ -407,8 +430,8 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   // same hint cost 5% (L = 385), so larger tiles keep the default policy.
   const bool w_once = BM <= 64 && m_tiles == 1;
   auto issue = [&](int kt, int stage, auto ext_c) {
-    const int soff = kt * BK * 2;
-    const int k0 = kt * BK, sb = w_tiled ? (k0 / 64) * 4096 + (k0 % 64) * 2 : soff;
+    const int soff = alay.ktile(kt, BK);
+    const int k0 = kt * BK, sb = w_tiled ? (k0 / 64) * 4096 + (k0 % 64) * 2 : k0 * 2;
     if (!loader) return;
     u32x4_t* base = lds + stage * STAGE;
 #pragma unroll
@@ -898,29 +921,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 // ---- launch helpers ---------------------------------------------------------------------
-template <int BM, int BN, int BKT, int WMW, int WNW, int S, bool PAIRED, class Map, class Epi>
+template <int BM, int BN, int BKT, int WMW, int WNW, int S, bool PAIRED, class Map, class Epi, class ALay>
 void launch_cfg(const GemmPlan& pl, const bf16_t* a, int lda, int M, int K, const bf16_t* w, int tiled, Map map,
-                int ncols, int nw, Epi epi, float* part, hipStream_t st) {
+                int ncols, int nw, Epi epi, float* part, hipStream_t st, ALay alay) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   constexpr int XR = gemm_extra_rows(BM, BN, BKT, WMW * WNW, PAIRED);
   // the extended-tile kernel only where the plan folds leftover rows into the
   // last row tile; the plain kernel keeps its smaller code and LDS otherwise
   if constexpr (XR > 0) {
     if (pl.ext) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, XR, PAIRED, Map, Epi>), dim3(grid),
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, XR, PAIRED, Map, Epi, ALay>), dim3(grid),
                          dim3(64 * WMW * WNW), 0, st, a, lda, M, K, w, nw, tiled, map, ncols, epi, part, nw,
-                         pl.m_tiles, pl.n_tiles, pl.splits);
+                         pl.m_tiles, pl.n_tiles, pl.splits, alay);
       return;
     }
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, 0, PAIRED, Map, Epi>), dim3(grid), dim3(64 * WMW * WNW),
-                     0, st, a, lda, M, K, w, nw, tiled, map, ncols, epi, part, nw, pl.m_tiles, pl.n_tiles, pl.splits);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BKT, WMW, WNW, S, 0, PAIRED, Map, Epi, ALay>), dim3(grid),
+                     dim3(64 * WMW * WNW), 0, st, a, lda, M, K, w, nw, tiled, map, ncols, epi, part, nw, pl.m_tiles,
+                     pl.n_tiles, pl.splits, alay);
 }
 
-template <bool PAIRED, class Map, class Epi>
+template <bool PAIRED, class Map, class Epi, class ALay = APlain>
 hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int K, const Wt& W, Map map,
                          int ncols, int nw, Epi epi, float* partial, hipStream_t st, const char* tag,
-                         bool reduce = true) {
+                         bool reduce = true, ALay alay = {}) {
   const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
   if (grid == 0) return hipSuccess;
   // buffer descriptors address at most 4 GiB per operand
@@ -934,7 +958,8 @@ hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int 
     ProfScope prof(tag, st);
     switch (pl.cfg) {
 #define FPD_CFG(E, BM, BN, BKT, WMW, WNW, S) \
-  case E: launch_cfg<BM, BN, BKT, WMW, WNW, S, PAIRED>(pl, a, lda, M, K, w, tiled, map, ncols, nw, epi, part, st); break;
+  case E: launch_cfg<BM, BN, BKT, WMW, WNW, S, PAIRED>(pl, a, lda, M, K, w, tiled, map, ncols, nw, epi, part, st, alay); \
+    break;
       FPD_GEMM_CFGS(FPD_CFG)
 #undef FPD_CFG
       default: return hipErrorInvalidValue;
@@ -949,15 +974,15 @@ hipError_t run_bf16_plan(const GemmPlan& pl, const void* A, int lda, int M, int 
   return hipGetLastError();
 }
 
-template <bool PAIRED, class Map, class Epi>
+template <bool PAIRED, class Map, class Epi, class ALay = APlain>
 hipError_t run_bf16(const void* A, int lda, int M, int K, const Wt& W, Map map, int ncols, int nw, Epi epi,
-                    float* partial, size_t partial_bytes, hipStream_t st, const char* tag) {
+                    float* partial, size_t partial_bytes, hipStream_t st, const char* tag, ALay alay = {}) {
   GemmPlan pl = plan_gemm_bf16(M, ncols, K, nw, PAIRED);
   if (pl.splits > 1 && pl.partial_floats * sizeof(float) > partial_bytes) {
     pl.splits = 1;
     pl.partial_floats = 0;
   }
-  return run_bf16_plan<PAIRED>(pl, A, lda, M, K, W, map, ncols, nw, epi, partial, st, tag);
+  return run_bf16_plan<PAIRED>(pl, A, lda, M, K, W, map, ncols, nw, epi, partial, st, tag, true, alay);
 }
 
 template <bool PAIRED, class Map, class Epi>
@@ -1084,6 +1109,13 @@ hipError_t gemm_store_f32(int dt, const void* A, int lda, int M, int K, const Wt
   if (dt == FPD_DTYPE_BF16)
     return run_bf16<false>(A, lda, M, K, W, MapPlain{}, N, N, e, partial, partial_bytes, st, tag);
   return run_f32<false>(A, lda, M, K, W, MapPlain{}, N, e, st, tag);
+}
+
+hipError_t gemm_store_fused_f32(const void* feats, int B, int n_t, int C, int H, const Wt& W, int N, float* out,
+                                int ldo, float* partial, size_t partial_bytes, hipStream_t st, const char* tag) {
+  EpiStore e{out, ldo};
+  return run_bf16<false>(feats, n_t * H, B * C, n_t * H, W, MapPlain{}, N, N, e, partial, partial_bytes, st, tag,
+                         AFused{C, H});
 }
 
 hipError_t gemm_residual(int dt, const void* A, int lda, int M, int K, const Wt& W, int N,
