@@ -132,7 +132,8 @@ FuseWs plan_fuse(const fpd_drafter& d, int B, int C) {
     off += al(bytes);
     return o;
   };
-  w.x = take(c.n_fused > 1 ? M * c.n_fused * H * e : 0);
+  // bf16 reads the features in place; f32 concatenates them first
+  w.x = take(c.n_fused > 1 && c.dtype != FPD_DTYPE_BF16 ? M * c.n_fused * H * e : 0);
   w.z = take(M * H * 4);
   w.zn = take(M * H * e);
   size_t pb = gemm_partial_bytes(c.dtype, (int)M, c.hidden, c.n_fused * c.hidden, c.hidden, false);
