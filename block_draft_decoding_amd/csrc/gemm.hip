@@ -305,9 +305,12 @@ __device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, i
 //
 // When M = k BM + r with 0 < r <= XR, the last row tile also carries the r
 // leftover rows (an (XR x BK) A slab after its BM rows in each stage, filled
-// by 4-byte LDS-writing loads, multiplied by 16x16x32 MFMAs whose columns are
-// split over all waves).  A separate row tile for them would stream the whole
-// weight column once more from HBM for r rows of work.
+// by one 16-byte LDS-writing load per loading wave, multiplied by 16x16x32
+// MFMAs whose columns are split over all waves).  A separate row tile for
+// them would stream the whole weight column once more from HBM for r rows of
+// work.  Two 4-byte loads per wave filled the slab at first: the same bytes,
+// but twice the load instructions, and the 385-row gate/up projection took
+// ~1 us longer per launch.
 // Addressing of the A operand (byte offsets for the buffer loads: a per-row
 // part fixed per lane, and a per-K-tile part that is scalar).  APlain: row-
 // major A [M, K], row m at m * lda.  AFused: the per-layer target features
@@ -356,10 +359,11 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   static_assert(STAGES >= 2 && STAGES <= 8 && LPS * (STAGES - 1) < 64, "pipeline depth");
   constexpr int CPT = PAIRED ? BN / 2 : BN;  // logical columns per tile
   static_assert(XR == 0 || XR == gemm_extra_rows(BM, BN, BK, NW, PAIRED), "extra rows of this tile shape");
-  constexpr int XI = XR * BK * 2 / (LW * 256);  // 4-byte loads per wave and stage for the extra rows
   constexpr int XB = XR ? CPT / (NW * 16) : 0;  // 16-column blocks (pairs when PAIRED) per wave
   constexpr int XA = PAIRED ? 2 * XB : XB;      // their accumulators
-  static_assert(XR == 0 || (XI >= 1 && XI * LW * 256 == XR * BK * 2 && XB * NW * 16 == CPT), "extra rows");
+  // the extra rows' 128 slots per stage: one 16-byte load per loading wave,
+  // waves 2 and 3 repeating the loads of waves 0 and 1
+  static_assert(XR == 0 || (XR * CH == 128 && LW % 2 == 0 && XB * NW * 16 == CPT), "extra rows");
   constexpr int AR = BM + XR;                // A rows held per stage
   constexpr int STAGE = (AR + BN) * CH;      // 16-byte slots per stage
 
@@ -414,15 +418,14 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
     boff[i] = w_tiled ? (uint32_t)((((size_t)(wrow / 32) * (K / 64) * 32 + wrow % 32) * 64 + c * 8) * 2)
                       : (uint32_t)(((size_t)wrow * K + c * 8) * 2);
   }
-  // extra rows: instruction i of a wave fills 16 slots (256 bytes); lane
-  // `lane` writes word lane % 4 of slot lane / 4
-  uint32_t xoff[XI > 0 ? XI : 1];
-#pragma unroll
-  for (int i = 0; i < XI; ++i) {
-    const int q = (wave * XI + i) * 16 + lane / 4, r = BM + q / CH;
+  // extra rows: lane l of a loading wave fills slot (wave & 1) * 64 + l of
+  // the XR x BK slab (rows past M clamped to M - 1, so two waves that fill
+  // the same slots write the same bytes)
+  uint32_t xoff;
+  {
+    const int q = (wave & 1) * 64 + lane, r = BM + q / CH;
     const int c = (q % CH) ^ ((r / (16 / CH)) & (CH - 1));
-    const int m = min(m0 + r, M - 1);
-    xoff[i] = alay.row(m, lda) + (uint32_t)(c * 16 + (lane & 3) * 4);
+    xoff = alay.row(min(m0 + r, M - 1), lda) + (uint32_t)(c * 16);
   }
   // With one row tile every weight tile is read by one workgroup only: the
   // small-row tiles then load it non-temporal (trajectory L = 25 block
@@ -445,8 +448,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
       for (int i = 0; i < BI; ++i) lds_dma16(brsrc, base + AR * CH + (wave * BI + i) * 64, boff[i], sb);
     }
     if constexpr (decltype(ext_c)::value) {
-#pragma unroll
-      for (int i = 0; i < XI; ++i) lds_dma4(arsrc, base + BM * CH + (wave * XI + i) * 16, xoff[i], soff);
+      lds_dma16(arsrc, base + BM * CH + (wave & 1) * 64, xoff, soff);
     }
   };
 
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   auto mainloop = [&](auto nr_c, auto ext_c) {
     constexpr int NR = decltype(nr_c)::value;
     constexpr bool EXT = decltype(ext_c)::value;
-    constexpr int LPSX = LPS + (EXT ? XI : 0);  // loads per wave and stage
+    constexpr int LPSX = LPS + (EXT ? 1 : 0);  // loads per wave and stage
     constexpr int KS = BK / 16;
     bf16x8_t af[2][TM > 0 ? TM : 1], bfv[2][TN];
     // extra rows: fragments of the two 32-deep K steps of a K-tile (j = kk / 2)

@@ -21,13 +21,6 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, u32x4_t* dst
 #endif
 }
 
-// The same with 4 bytes per lane: lane i fills dst + 4 i bytes.
-__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, u32x4_t* dst, uint32_t voff, int soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, voff, soff, 0, 0);
-#endif
-}
-
 template <int CH>  // 16-byte chunks per row (BK / 8)
 __device__ __forceinline__ int swz(int r, int c) {
   return r * CH + (c ^ ((r / (16 / CH)) & (CH - 1)));
