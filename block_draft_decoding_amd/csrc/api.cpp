@@ -43,6 +43,28 @@ int round8(int x) { return (x + 7) & ~7; }
 constexpr int64_t kMaxRows = int64_t(1) << 24;
 bool too_many_rows(int32_t B, int32_t n) { return (int64_t)B * n > kMaxRows; }
 
+// The bf16 kernels read every operand through a buffer descriptor whose
+// byte range is 32 bits wide, so no single operand of a call may reach
+// 4 GiB: per call, the widest activation rows times the row count (drafter
+// forward: normed hidden, attention output and SwiGLU output rows of B x L
+// positions; context fusion: the n_t layers' feature rows of B x C
+// positions; LM head: hidden rows of B x (L - 1) positions), and per drafter
+// each weight matrix (rows padded to 32 in the K-tile-contiguous copies).
+constexpr int64_t kMaxOperandBytes = 0xffffffffll;
+int64_t forward_row_bytes(const fpd_config& c) {
+  return c.dtype == FPD_DTYPE_BF16 ? (int64_t)std::max({c.hidden, c.n_q * c.head_dim, c.inter}) * 2 : 0;
+}
+int64_t fusion_row_bytes(const fpd_config& c) {
+  return c.dtype == FPD_DTYPE_BF16 ? (int64_t)c.n_fused * c.hidden * 2 : 0;
+}
+bool over_4gib(int64_t rows, int64_t row_bytes) { return rows * row_bytes > kMaxOperandBytes; }
+int64_t widest_weight_bytes(const fpd_config& c) {
+  auto w = [](int64_t rows, int64_t k) { return (rows + 31) / 32 * 32 * k * 2; };
+  const int64_t q = (int64_t)c.n_q * c.head_dim, kv = (int64_t)c.n_kv * c.head_dim, H = c.hidden;
+  return std::max({w(q + 2 * kv, H), w(H, q), w(2 * (int64_t)c.inter, H), w(H, c.inter),
+                   w(H, (int64_t)c.n_fused * H), w(c.vocab, H)});
+}
+
 }  // namespace
 
 struct fpd_drafter {
@@ -213,6 +235,8 @@ int32_t fpd_drafter_create(const fpd_config* cfg, const fpd_weights* w, fpd_draf
     return fail(FPD_E_UNSUPPORTED, "bf16 drafters need head_dim 128");
   if (c.dtype == FPD_DTYPE_F32 && c.head_dim != 64 && c.head_dim != 128)
     return fail(FPD_E_UNSUPPORTED, "f32 drafters need head_dim 64 or 128");
+  if (c.dtype == FPD_DTYPE_BF16 && widest_weight_bytes(c) > kMaxOperandBytes)
+    return fail(FPD_E_UNSUPPORTED, "a bf16 weight matrix of 4 GiB or more");
   if (!w->w_fc || !w->g_fc || !w->embed || !w->w_lm || !w->g_final || !w->layers)
     return fail(FPD_E_ARG, "null weight pointer");
   for (int i = 0; i < c.n_layers; ++i) {
@@ -404,6 +428,8 @@ int32_t fpd_workspace_size(const fpd_drafter* d, int32_t B, int32_t C, int32_t L
   if (!d || !bytes) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || C < 0 || L < 2) return fail(FPD_E_SHAPE, "need B >= 1, C >= 0, L >= 2");
   if (too_many_rows(B, C) || too_many_rows(B, L)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
+  if (over_4gib((int64_t)B * L, forward_row_bytes(d->cfg)) || over_4gib((int64_t)B * C, fusion_row_bytes(d->cfg)))
+    return fail(FPD_E_UNSUPPORTED, "a bf16 operand of 4 GiB or more (too many rows for one call)");
   // LM-head partials: wide chunks of the whole vocabulary, or narrow chunks,
   // which are used only while the wide ones number under 128 per launch
   // (at most 4 x 127 narrow chunks in a row)
@@ -473,6 +499,8 @@ int32_t fpd_fuse_context_kv(const fpd_drafter* d, const void* feats, int32_t B, 
   if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || C < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C >= 1, pos0 >= 0");
   if (too_many_rows(B, C)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
+  if (over_4gib((int64_t)B * C, fusion_row_bytes(d->cfg)))
+    return fail(FPD_E_UNSUPPORTED, "bf16 features of 4 GiB or more (too many rows for one call)");
   if (ctx_cap < C || ctx_cap % 8) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
   return fuse_rows(d, feats, B, C, pos0, (char*)ctx_k, (char*)ctx_v, ctx_cap, ws, ws_bytes, stream);
 }
@@ -483,6 +511,8 @@ int32_t fpd_append_context_kv(const fpd_drafter* d, const void* feats, int32_t B
   if (!d || !feats || !ctx_k || !ctx_v) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || C_new < 1 || pos0 < 0) return fail(FPD_E_SHAPE, "need B >= 1, C_new >= 1, pos0 >= 0");
   if (too_many_rows(B, C_new)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
+  if (over_4gib((int64_t)B * C_new, fusion_row_bytes(d->cfg)))
+    return fail(FPD_E_UNSUPPORTED, "bf16 features of 4 GiB or more (too many rows for one call)");
   if (ctx_cap % 8 || (int64_t)pos0 + C_new > ctx_cap)
     return fail(FPD_E_SHAPE, "ctx_cap must be a multiple of 8 and hold pos0 + C_new keys");
   // key row pos0 of every (layer, b, kv head) segment: the K rows are d
@@ -502,6 +532,8 @@ int32_t draft_impl(const fpd_drafter* d, const int32_t* tokens, int32_t B, int32
   if (!d || !tokens || !hidden_out) return fail(FPD_E_ARG, "null argument");
   if (B < 1 || L < 2 || C < 0 || block_pos < 0) return fail(FPD_E_SHAPE, "need B >= 1, L >= 2, C >= 0, block_pos >= 0");
   if (too_many_rows(B, L) || too_many_rows(B, C)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
+  if (over_4gib((int64_t)B * L, forward_row_bytes(d->cfg)))
+    return fail(FPD_E_UNSUPPORTED, "a bf16 activation of 4 GiB or more (too many rows for one call)");
   if (C > 0 && (!ctx_k || !ctx_v)) return fail(FPD_E_ARG, "null context");
   if (C > 0 && (ctx_cap < C || ctx_cap % 8)) return fail(FPD_E_SHAPE, "ctx_cap must be >= C and a multiple of 8");
   const DraftWs w = plan_draft(*d, B, L, C);
@@ -623,6 +655,8 @@ int32_t fpd_constrained_argmax(const fpd_drafter* d, const fpd_layout* lay, cons
   if (lay->d != d) return fail(FPD_E_ARG, "layout was created for another drafter");
   if (B < 1) return fail(FPD_E_SHAPE, "need B >= 1");
   if (too_many_rows(B, lay->host.L)) return fail(FPD_E_SHAPE, "more than 2^24 rows");
+  if (d->cfg.dtype == FPD_DTYPE_BF16 && over_4gib((int64_t)B * (lay->host.L - 1), (int64_t)d->cfg.hidden * 2))
+    return fail(FPD_E_UNSUPPORTED, "bf16 hidden states of 4 GiB or more (too many rows for one call)");
   const HostLayout& h = lay->host;
   const fpd_config& c = d->cfg;
   const int L = h.L, ns = h.n_sets();

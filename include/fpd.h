@@ -49,6 +49,12 @@
  *     of each device's static scratch address (read under a lock).
  *   - fpd_last_error() is thread-local and describes the most recent
  *     failing call on the calling thread.
+ *   - Size limits: at most 2^24 rows (B x positions) per call, and for BF16
+ *     drafters no operand of 4 GiB or more (the kernels address each
+ *     operand through a 32-bit byte range): B*L*max(H, n_q*d, I)*2 bytes in
+ *     the drafter forward, B*C*n_fused*H*2 in context fusion, B*(L-1)*H*2 in
+ *     the LM head, and each weight matrix at creation.  Calls beyond them
+ *     return FPD_E_SHAPE (rows) or FPD_E_UNSUPPORTED (bytes) before any work.
  */
 #ifndef FPD_H
 #define FPD_H
@@ -69,7 +75,8 @@ enum {
   FPD_E_DTYPE = 3,        /* unknown dtype                                    */
   FPD_E_SCHEMA = 4,       /* schema expands to an invalid layout              */
   FPD_E_WORKSPACE = 5,    /* workspace smaller than fpd_workspace_size()      */
-  FPD_E_UNSUPPORTED = 6,  /* a shape the kernels do not implement             */
+  FPD_E_UNSUPPORTED = 6,  /* a shape the kernels do not implement, or a bf16 */
+                          /* operand of 4 GiB or more                        */
   FPD_E_HIP = 7           /* HIP runtime error (allocation, launch)           */
 };
 

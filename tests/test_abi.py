@@ -117,6 +117,8 @@ def _fake_weights(n_layers):
     (dict(hidden=100), fpd.FPD_E_UNSUPPORTED),
     (dict(head_dim=32), fpd.FPD_E_UNSUPPORTED),
     (dict(dtype=1, head_dim=64), fpd.FPD_E_UNSUPPORTED),
+    # a bf16 LM head of 524,320 x 4,096 x 2 bytes (4 GiB or more)
+    (dict(dtype=1, head_dim=128, hidden=4096, vocab=524320), fpd.FPD_E_UNSUPPORTED),
 ])
 def test_drafter_create_errors(over, code):
     c = _cfg(**over)
@@ -188,3 +190,37 @@ def test_workspace_grows_with_the_problem():
         assert sizes[0] < sizes[1] < sizes[2] < (8 << 30)
     finally:
         fpd._destroy(h)
+
+
+def test_bf16_operands_of_4_gib_are_refused_before_any_work():
+    # hidden 256, n_q * d = 512, I = 704: the forward's widest rows (SwiGLU
+    # output) are 1,408 bytes, the two fused layers' feature rows 1,024
+    # bytes, so row counts under 2^24 can still reach 4 GiB in one operand
+    c = _cfg(dtype=1, head_dim=128)
+    w, keep = _fake_weights(c.n_layers)
+    h = ctypes.c_void_p()
+    assert fpd._create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == fpd.FPD_OK
+    try:
+        n = ctypes.c_size_t()
+        # forward: 4,096 x 1,024 positions = 5.9 GB of SwiGLU rows; 4,096 x 700 = 4.04 GB
+        assert fpd._ws_size(h, 1 << 12, 0, 1 << 10, ctypes.byref(n)) == fpd.FPD_E_UNSUPPORTED
+        assert fpd._ws_size(h, 1 << 12, 0, 700, ctypes.byref(n)) == fpd.FPD_OK
+        assert fpd._draft(h, 8, 1 << 12, 1 << 10, None, None, 0, 0, 0, 8, None, 0, None) == fpd.FPD_E_UNSUPPORTED
+        assert "4 GiB" in fpd.fpd_last_error()
+        # fusion: 4,096 x 1,024 positions = exactly 2^32 bytes of features; 4,096 x 1,000 fit
+        assert fpd._ws_size(h, 1 << 12, 1 << 10, 16, ctypes.byref(n)) == fpd.FPD_E_UNSUPPORTED
+        assert fpd._ws_size(h, 1 << 12, 1000, 16, ctypes.byref(n)) == fpd.FPD_OK
+        assert fpd._fuse(h, 8, 1 << 12, 1 << 10, 0, 8, 8, 1 << 10, None, 0, None) == fpd.FPD_E_UNSUPPORTED
+        assert fpd._append(h, 8, 1 << 12, 1 << 10, 0, 8, 8, 1 << 10, None, 0, None) == fpd.FPD_E_UNSUPPORTED
+    finally:
+        fpd._destroy(h)
+    # the same shapes are fine for an f32 drafter, whose kernels use plain addressing
+    c32 = _cfg()
+    w32, keep32 = _fake_weights(c32.n_layers)
+    h32 = ctypes.c_void_p()
+    assert fpd._create(ctypes.byref(c32), ctypes.byref(w32), ctypes.byref(h32)) == fpd.FPD_OK
+    try:
+        n = ctypes.c_size_t()
+        assert fpd._ws_size(h32, 1 << 12, 1 << 10, 1 << 10, ctypes.byref(n)) == fpd.FPD_OK
+    finally:
+        fpd._destroy(h32)
