@@ -154,6 +154,19 @@ def test_more_than_eight_split_partials():
     compare_all(wl, g, lg, res, "bf16", "16-way split-K sums", inp.weights.w_lm)
 
 
+def test_folded_rows_fill_both_halves_of_the_extra_slab():
+    """A wide MLP (I = 9,728: 76 paired column tiles) over 396 block rows =
+    3 x 128 + 12: the gate/up projection carries the 12 leftover rows in its
+    last row tile.  The 16-row slab of extra rows is filled by two different
+    loading waves, 8 rows each, so 12 rows use both halves with the second
+    one partly clamped (1 and 16 leftover rows are the 385-row and the
+    16 x 25-row full-size blocks)."""
+    shape = replace(SMALL, inter=9728)
+    wl = small_workload("text", 1, 64, seed=91, shape=shape, block_len=396)
+    inp, g, lg, res = run_both(wl)
+    compare_all(wl, g, lg, res, "bf16", "12 folded rows", inp.weights.w_lm)
+
+
 @pytest.mark.parametrize("n_layers", [1, 2, 3])
 def test_per_layer_hidden_parity(n_layers):
     shape = replace(SMALL, n_layers=3)
