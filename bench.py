@@ -345,7 +345,7 @@ def main():
             ach = nbytes / (avg_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
-        roof["traffic"] = profiling.read_traffic(dom)
+        roof["traffic"] = profiling.read_traffic(dom, args.workload)
         roof.update({"kernel": dom, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": kern[dom][0] // nprof,
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
     kernels = {t: {"launches_per_step": round(c[0] / nprof, 2), "ms_per_step": round(c[1] / nprof, 4)}

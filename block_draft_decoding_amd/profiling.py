@@ -122,7 +122,7 @@ def traffic_summary(args) -> str:
     f_fetch, f_write = kib / cf["mean"], kib / cw["mean"]
     fetch_b = fetch["mean"] * 1024.0 * f_fetch
     write_b = write["mean"] * 1024.0 * f_write
-    rec = {"tag": args.tag, "kernel_regex": args.kernel_regex, "fetch_bytes": round(fetch_b),
+    rec = {"tag": args.tag, "workload": args.workload, "kernel_regex": args.kernel_regex, "fetch_bytes": round(fetch_b),
            "write_bytes": round(write_b), "traffic_bytes": round(fetch_b + write_b),
            "copy_factor_fetch": round(f_fetch, 4), "copy_factor_write": round(f_write, 4),
            "source_files": list(kernel_files(args.tag) or ()), "source_digest": source_digest(kernel_files(args.tag))}
@@ -138,14 +138,15 @@ def traffic_summary(args) -> str:
              f"Scale factors (copy bytes / counter bytes): fetch {f_fetch:.4f}, write {f_write:.4f}.  "
              f"HBM traffic per launch: {fetch_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written = "
              f"{(fetch_b + write_b) / 1e6:.1f} MB.", "",
-             "Machine-readable record (bench.py reports `traffic` only while the kernel's source files have "
-             "this digest):", "", "```json", json.dumps(rec), "```"]
+             "Machine-readable record (bench.py reports `traffic` for this kernel and workload only while the "
+             "kernel's source files have this digest):", "", "```json", json.dumps(rec), "```"]
     return "\n".join(lines) + "\n"
 
 
-def read_traffic(tag: str, path: str = TRAFFIC_MD) -> Optional[int]:
-    """Measured HBM bytes per launch of `tag`, or None when no measurement
-    exists or the kernel's source files changed since it was taken."""
+def read_traffic(tag: str, workload: str, path: str = TRAFFIC_MD) -> Optional[int]:
+    """Measured HBM bytes per launch of `tag` in `workload`, or None when no
+    measurement of that kernel in that workload exists or the kernel's
+    source files changed since it was taken."""
     try:
         text = open(path).read()
     except OSError:
@@ -154,7 +155,9 @@ def read_traffic(tag: str, path: str = TRAFFIC_MD) -> Optional[int]:
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("tag") != tag or rec.get("source_digest") != source_digest(kernel_files(tag)):
+    if rec.get("tag") != tag or rec.get("workload") != workload:
+        return None
+    if rec.get("source_digest") != source_digest(kernel_files(tag)):
         return None
     return int(rec["traffic_bytes"])
 
@@ -170,6 +173,7 @@ def main(argv: Optional[List[str]] = None) -> int:
     s.add_argument("bench_json", nargs="?")
     t = sub.add_parser("traffic")
     t.add_argument("--tag", required=True)
+    t.add_argument("--workload", required=True, help="bench.py workload the counters were taken on")
     t.add_argument("--kernel-regex", required=True)
     t.add_argument("--copy-regex", default="copy|Copy|elementwise")
     t.add_argument("--fetch", required=True)
