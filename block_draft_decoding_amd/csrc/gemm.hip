@@ -311,25 +311,27 @@ __device__ __forceinline__ int gemm_tile_order(int bid, int grid, int m_tiles, i
 // work.  Two 4-byte loads per wave filled the slab at first: the same bytes,
 // but twice the load instructions, and the 385-row gate/up projection took
 // ~1 us longer per launch.
+//
 // Addressing of the A operand (byte offsets for the buffer loads: a per-row
 // part fixed per lane, and a per-K-tile part that is scalar).  APlain: row-
 // major A [M, K], row m at m * lda.  AFused: the per-layer target features
 // [B, n_t, C, H] read in place as their concatenation [B * C, n_t * H] (row
 // b * C + c, column t * H + k; lda = n_t * H), which the context fusion's
 // projection would otherwise copy out first (a 64-deep K tile never crosses
-// a layer, since H is a multiple of 64).
+// a layer, since H is a multiple of 64).  Both parts are unsigned 32-bit
+// byte offsets (operands stay under 4 GiB), added by the hardware.
 struct APlain {
   __device__ uint32_t row(int m, int lda) const { return (uint32_t)((size_t)m * lda * 2); }
-  __device__ int ktile(int kt, int bk) const { return kt * bk * 2; }
+  __device__ uint32_t ktile(int kt, int bk) const { return (uint32_t)(kt * bk * 2); }
 };
 struct AFused {
   int C, H;  // positions per request, columns of one target layer
   __device__ uint32_t row(int m, int lda) const {
     return (uint32_t)(((size_t)(m / C) * C * lda + (size_t)(m % C) * H) * 2);
   }
-  __device__ int ktile(int kt, int bk) const {
+  __device__ uint32_t ktile(int kt, int bk) const {
     const int k = kt * bk;
-    return (int)(((size_t)(k / H) * C * H + k % H) * 2);
+    return (uint32_t)(((size_t)(k / H) * C * H + k % H) * 2);
   }
 };
 
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_kernel(
   // same hint cost 5% (L = 385), so larger tiles keep the default policy.
   const bool w_once = BM <= 64 && m_tiles == 1;
   auto issue = [&](int kt, int stage, auto ext_c) {
-    const int soff = alay.ktile(kt, BK);
+    const int soff = (int)alay.ktile(kt, BK);  // the same 32 bits as a scalar offset
     const int k0 = kt * BK, sb = w_tiled ? (k0 / 64) * 4096 + (k0 % 64) * 2 : k0 * 2;
     if (!loader) return;
     u32x4_t* base = lds + stage * STAGE;
