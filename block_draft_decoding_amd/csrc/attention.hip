@@ -39,7 +39,7 @@ constexpr int KT = 64;          // keys per tile
 constexpr int D = 128;          // head dim of the bf16 path
 constexpr int AW = 8;           // waves per workgroup
 constexpr int QROWS = AW * 32;  // packed query rows per workgroup
-constexpr int AST = 3;          // depth of the global -> LDS ring (8-wave query tiles)
+constexpr int AST = 4;          // depth of the global -> LDS ring (8-wave query tiles; the array holds TST)
 constexpr int TST = 5;          // depth of the ring of the tail tile's workgroups
 constexpr int KSLOTS = KT * 16; // 16-byte chunks of a K tile (64 keys x 256 bytes)
 constexpr int VSLOTS = D * 8;   // 16-byte chunks of a V^T tile (128 dims x 64 keys)
